@@ -1,0 +1,53 @@
+"""Write oracle_regression.txt: a regression lock on the oracle's output.
+
+Calls only ``oracle/`` (and ``workloads`` for the seeded inputs).  The stored
+values are not a pin of correctness -- the pages print no worked example --
+they only make any later change to the oracle's arithmetic visible.
+
+Run from the repository root:  python tests/golden/make_oracle_regression.py
+"""
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+
+OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_regression.txt")
+CASES = [  # (style, x dtype, cos dtype, cos layout, head_dim)
+    ("interleaved", "bf16", "fp32", "shared", 64),
+    ("rotate_half", "fp16", "fp32", "per_head", 128),
+    ("interleaved", "fp16", "bf16", "shared", 128),
+]
+
+
+def cases():
+    for style, xdt, cdt, lay, d in CASES:
+        T, H = 3, 2
+        qkv = wl.fused_qkv(4242, T, H, d, xdt)
+        qg, kg = wl.norm_weights(4242, d)
+        c, s = wl.rope_tables(np.arange(T) * 37, (d // 2,), d, style, dtype=cdt)
+        if lay == "per_head":
+            c, s = wl.expand_per_head(c, H), wl.expand_per_head(s, H)
+        to_np = (lambda t: t.numpy()) if cdt == "fp32" else wl.u16
+        q, k = oracle.fused_qk(wl.u16(qkv), xdt, heads=H, head_dim=d, q_gamma=qg.numpy(),
+                               k_gamma=kg.numpy(), eps=wl.EPS, cos=to_np(c), sin=to_np(s),
+                               cos_dtype=cdt, cos_layout=lay, style=style)
+        yield "%s %s %s %s %d" % (style, xdt, cdt, lay, d), np.concatenate([q.ravel(), k.ravel()])
+
+
+def main():
+    with open(OUT, "w") as f:
+        f.write("# oracle regression lock; written by make_oracle_regression.py\n")
+        for name, vals in cases():
+            f.write("case %s\n" % name)
+            for i in range(0, vals.size, 97):      # every 97th value, as exact hex
+                f.write("%d %s\n" % (i, float(vals[i]).hex()))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,81 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), builds it, and runs the pin tests against that
+build: at least one pin has to fail.  This shows the pins constrain every
+step of the oracle: decode, sum of squares, mean, eps, weight, table index,
+partner index, sign, rounding.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import tests.test_oracle_pins as pins
+
+MUTATIONS = {
+    "drop_last_square": ("sum_sq += v[d] * v[d];", "if (d + 1 < D) sum_sq += v[d] * v[d];"),
+    "sum_not_mean": ("sum_sq / (double)D", "sum_sq"),
+    "eps_outside_root": ("1.0 / sqrt(ms + eps64)", "1.0 / sqrt(ms) + eps64"),
+    "gamma_reversed": ("(double)gamma[d]", "(double)gamma[D - 1 - d]"),
+    "first_sign": ("oh[a] = nrm[a] * ca - nrm[b] * sa;", "oh[a] = nrm[a] * ca + nrm[b] * sa;"),
+    "both_signs": ("oh[a] = nrm[a] * ca - nrm[b] * sa;\n                oh[b] = nrm[b] * cb + nrm[a] * sb;",
+                   "oh[a] = nrm[a] * ca + nrm[b] * sa;\n                oh[b] = nrm[b] * cb - nrm[a] * sb;"),
+    "cos_of_first_for_both": ("cb = table_value(cos, cos_dtype, row * D + b)",
+                              "cb = table_value(cos, cos_dtype, row * D + a)"),
+    "sin_of_second_for_both": ("sa = table_value(sin, cos_dtype, row * D + a)",
+                               "sa = table_value(sin, cos_dtype, row * D + b)"),
+    "cos_sin_swapped": ("ca = table_value(cos,", "ca = table_value(sin,"),
+    "per_head_row_transposed": ("t * heads + h;", "t + h * heads;"),
+    "rotate_half_partner": ("b = i + half;", "b = D - 1 - i;"),
+    "fp16_subnormal_scale": ("ldexp((double)m / 1024.0, -14)", "ldexp((double)m / 1024.0, -15)"),
+    "bf16_bias": ("1.0 + (double)m / 128.0, e - 127", "1.0 + (double)m / 128.0, e - 126"),
+    "round_ties_away": ("rint(a / q)", "round(a / q)"),
+    "gamma_after_rope_missing": ("nrm[d] = v[d] * r * (double)gamma[d];", "nrm[d] = v[d] * r;"),
+}
+
+PIN_TESTS = [
+    (pins.test_decode_bf16_exhaustive, {}),
+    (pins.test_decode_fp16_exhaustive, {}),
+    (pins.test_round_fp16_matches_numpy, {}),
+    (pins.test_round_bf16_properties, {}),
+    (pins.test_norm_matches_torch_rms_norm, {"x_dtype": "fp16", "head_dim": 64}),
+    (pins.test_interleaved_is_complex_multiply, {}),
+    (pins.test_rotate_half_textbook_form, {}),
+    (pins.test_rms_closed_form, {}),
+    (pins.test_styles_agree_under_permutation, {}),
+    (pins.test_pair_norm_identity, {"style": "interleaved"}),
+    (pins.test_brute_force_fused_qkv, {"style": "rotate_half", "cos_layout": "per_head",
+                                       "x_dtype": "bf16", "cos_dtype": "fp32", "head_dim": 64}),
+]
+
+
+def _caught(variant) -> list:
+    caught = []
+    for fn, kw in PIN_TESTS:
+        try:
+            with np.errstate(all="ignore"):
+                fn(variant, **kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+    return caught
+
+
+def test_unmutated_source_passes_every_pin():
+    assert _caught(oracle.default()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    mutated = src.replace(old, new, 1)
+    path = os.path.join(tmp_path, "mut.c")
+    with open(path, "w") as f:
+        f.write(mutated)
+    lib = oracle.compile_source(path, os.path.join(tmp_path, "libmut.so"))
+    caught = _caught(oracle.Oracle(lib))
+    assert caught, "no pin catches mutation " + name

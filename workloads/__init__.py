@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for the fused DiT QK-norm + RoPE pass.
+
+This module holds none of the pass's own arithmetic: it draws activations and
+norm weights and builds RoPE cos/sin tables from token positions.  The HIP
+path's tests and bench and the CPU oracle's tests all take their inputs from
+here, so both sides see identical bits.
+
+Shapes, distributions and position grids stand in for the activations of the
+two models the source pages measure on (Wan A14B video, FLUX.2-dev images);
+no model weights or datasets are involved.
+
+Recipe (every workload):
+  * root seed ``1000 + k`` for workload k = 1..5, split with
+    ``numpy.random.SeedSequence.spawn`` into: per-token scale, activations
+    (one child per block of ``ROWS_PER_BLOCK`` tokens, so the draw does not
+    depend on the number of threads), q_gamma, k_gamma;
+  * per-token scale ``s_t = exp(U[ln 0.1, ln 10])`` multiplies the whole
+    activation row (Q, K and V alike) in fp32, then one RNE cast to bf16/fp16;
+  * ``gamma = 1 + 0.1 N(0,1)`` in fp32, separately for Q and K;
+  * cos/sin from integer positions: per axis a with n_a frequency pairs,
+    ``freq_j = theta ** (-j / n_a)`` (j = 0..n_a-1), pair index axis-major,
+    angle = pos * freq in fp64, cos/sin in fp64 rounded once to fp32; a bf16
+    table is the RNE of that fp32 table.  Interleaved tables repeat each
+    pair's value at dims (2i, 2i+1); rotate-half tables at (i, i + D/2).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+THETA = 10000.0
+EPS = 1e-6
+ROWS_PER_BLOCK = 512
+
+DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: tensor layout, sizes and RoPE position grid."""
+
+    key: str
+    seed: int
+    layout: str              # "fused": one [T, 3*H*D] QKV buffer; "separate": q, k [T, H, D]
+    tokens: int
+    heads: int
+    head_dim: int
+    dtypes: tuple
+    styles: tuple
+    cos_layouts: tuple
+    grid: tuple              # position grid (row-major), one entry per axis
+    split: tuple             # frequency pairs per axis; sums to head_dim / 2
+    text_tokens: int = 0     # leading tokens all at position 0 on every axis
+    note: str = field(default="", compare=False)
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", 1001, "fused", 256, 24, 64, ("bf16",), ("interleaved",), ("shared",),
+        (256,), (32,), note="1-D positions 0..255"),
+    "mid": Workload(
+        "mid", 1002, "fused", 4096, 24, 128, ("bf16",), ("rotate_half",),
+        ("shared", "per_head"), (64, 64), (32, 32), note="2-D 64x64 grid"),
+    "flux": Workload(
+        "flux", 1003, "separate", 4608, 48, 128, ("fp16", "bf16"), ("interleaved",),
+        ("shared",), (1, 64, 64), (22, 21, 21), text_tokens=512,
+        note="512 text tokens at the origin, then a 64x64 image grid"),
+    "headline": Workload(
+        "headline", 1004, "fused", 32760, 40, 128, ("bf16",), ("interleaved",),
+        ("shared",), (21, 30, 52), (22, 21, 21), note="Wan A14B 21x30x52 latent grid"),
+    "large": Workload(
+        "large", 1005, "fused", 75600, 40, 128, ("bf16",),
+        ("interleaved", "rotate_half"), ("shared", "per_head"), (21, 45, 80), (22, 21, 21),
+        note="21x45x80 latent grid"),
+}
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def positions(w: Workload) -> np.ndarray:
+    """Integer positions [tokens, n_axes], row-major over ``w.grid``."""
+    axes = [np.arange(n, dtype=np.int64) for n in w.grid]
+    mesh = np.meshgrid(*axes, indexing="ij")
+    grid_pos = np.stack([m.reshape(-1) for m in mesh], axis=1)
+    text = np.zeros((w.text_tokens, len(w.grid)), dtype=np.int64)
+    pos = np.concatenate([text, grid_pos], axis=0)
+    assert pos.shape[0] == w.tokens, (pos.shape, w.tokens)
+    return pos
+
+
+def rope_tables(pos: np.ndarray, split: tuple, head_dim: int, style: str,
+                theta: float = THETA, dtype: str = "fp32"):
+    """cos, sin tables [tokens, head_dim] as CPU torch tensors (fp32 or bf16)."""
+    pos = np.asarray(pos, dtype=np.int64)
+    if pos.ndim == 1:
+        pos = pos[:, None]
+    assert pos.shape[1] == len(split) and 2 * sum(split) == head_dim
+    angles = []
+    for a, n_a in enumerate(split):
+        freq = theta ** (-np.arange(n_a, dtype=np.float64) / n_a)
+        angles.append(pos[:, a:a + 1].astype(np.float64) * freq[None, :])
+    ang = np.concatenate(angles, axis=1)                      # [T, D/2], fp64
+    c_pair = np.cos(ang).astype(np.float32)
+    s_pair = np.sin(ang).astype(np.float32)
+    if style == "interleaved":
+        cos = np.repeat(c_pair, 2, axis=1)
+        sin = np.repeat(s_pair, 2, axis=1)
+    elif style == "rotate_half":
+        cos = np.concatenate([c_pair, c_pair], axis=1)
+        sin = np.concatenate([s_pair, s_pair], axis=1)
+    else:
+        raise ValueError(style)
+    cos_t = torch.from_numpy(np.ascontiguousarray(cos))
+    sin_t = torch.from_numpy(np.ascontiguousarray(sin))
+    if dtype == "bf16":
+        cos_t, sin_t = cos_t.to(torch.bfloat16), sin_t.to(torch.bfloat16)
+    elif dtype != "fp32":
+        raise ValueError(dtype)
+    return cos_t, sin_t
+
+
+def expand_per_head(table: torch.Tensor, heads: int) -> torch.Tensor:
+    """Materialise a shared [T, D] table as the per-head layout [T, heads, D]."""
+    return table[:, None, :].expand(table.shape[0], heads, table.shape[1]).contiguous()
+
+
+def _children(seed: int):
+    root = np.random.SeedSequence(seed)
+    return root.spawn(4)   # scale, activations, q_gamma, k_gamma
+
+
+def token_scales(seed: int, tokens: int) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(_children(seed)[0]))
+    return np.exp(g.uniform(math.log(0.1), math.log(10.0), size=tokens)).astype(np.float32)
+
+
+def norm_weights(seed: int, head_dim: int):
+    """(q_gamma, k_gamma), each fp32 [head_dim] = 1 + 0.1 N(0,1)."""
+    kids = _children(seed)
+    out = []
+    for child in kids[2:4]:
+        g = np.random.Generator(np.random.PCG64(child))
+        gam = (1.0 + 0.1 * g.standard_normal(head_dim)).astype(np.float32)
+        out.append(torch.from_numpy(gam))
+    return tuple(out)
+
+
+def _normal_rows(seed: int, tokens: int, width: int, scale: np.ndarray) -> np.ndarray:
+    """fp32 [tokens, width] = N(0,1) * scale[t], drawn block by block."""
+    out = np.empty((tokens, width), dtype=np.float32)
+    n_blocks = -(-tokens // ROWS_PER_BLOCK) if tokens else 0
+    blocks = _children(seed)[1].spawn(n_blocks) if n_blocks else []
+
+    def work(b):
+        lo = b * ROWS_PER_BLOCK
+        hi = min(tokens, lo + ROWS_PER_BLOCK)
+        g = np.random.Generator(np.random.PCG64(blocks[b]))
+        g.standard_normal((hi - lo, width), dtype=np.float32, out=out[lo:hi])
+        out[lo:hi] *= scale[lo:hi, None]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(n_blocks)))
+    return out
+
+
+def _cast(a: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(a).to(DTYPES[dtype])
+
+
+def fused_qkv(seed: int, tokens: int, heads: int, head_dim: int, dtype: str) -> torch.Tensor:
+    """Fused activation buffer [tokens, 3*heads*head_dim] (Q | K | V)."""
+    s = token_scales(seed, tokens)
+    return _cast(_normal_rows(seed, tokens, 3 * heads * head_dim, s), dtype)
+
+
+def separate_qk(seed: int, tokens: int, heads: int, head_dim: int, dtypes=("bf16",)):
+    """Per-tensor q and k [tokens, heads, head_dim] for each requested dtype.
+
+    One fp32 draw [tokens, 2*heads*head_dim] (q then k per token) is cast to
+    every dtype, so the fp16 and bf16 tensors hold the same underlying values.
+    """
+    s = token_scales(seed, tokens)
+    raw = _normal_rows(seed, tokens, 2 * heads * head_dim, s)
+    raw = raw.reshape(tokens, 2, heads, head_dim)
+    out = {}
+    for dt in dtypes:
+        q = _cast(np.ascontiguousarray(raw[:, 0]), dt)
+        k = _cast(np.ascontiguousarray(raw[:, 1]), dt)
+        out[dt] = (q, k)
+    return out
+
+
+def workload_tables(w: Workload, style: str, dtype: str = "fp32"):
+    return rope_tables(positions(w), w.split, w.head_dim, style, dtype=dtype)
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    """The raw 16-bit pattern of a bf16/fp16 CPU tensor, as a numpy uint16 view."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def algorithmic_bytes(tokens: int, heads: int, head_dim: int, n_tensors: int = 2,
+                      x_bytes: int = 2, cos_layout: str = "shared", cos_bytes: int = 4) -> int:
+    """Bytes the pass must move: Q/K read + written, cos and sin read once."""
+    qk = tokens * n_tensors * heads * head_dim * x_bytes * 2
+    rows = tokens * (heads if cos_layout == "per_head" else 1)
+    return qk + rows * head_dim * cos_bytes * 2
