@@ -1,0 +1,226 @@
+"""Benchmark of the fused QK-norm + RoPE pass on one MI355X.
+
+One step = one call of the pass over the whole workload (every Q and K head
+of every token), in place on a device-resident fused QKV buffer.  Default
+workload: Wan-A14B-shaped 32760 tokens x 3*40*128 bf16, interleaved RoPE,
+one shared fp32 cos/sin row per token.
+
+Prints ONE JSON line.  ``value`` is achieved algorithmic HBM throughput over
+the K timed steps (GB/s, bytes the pass must move / time);
+``roofline.achieved`` uses the mean kernel duration from HIP events recorded
+around each launch on the launch stream; ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+                  [--layout shared|per_head] [--style interleaved|rotate_half]
+                  [--no-cpu-baseline] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QK-norm+RoPE µs/call and achieved HBM GB/s (% of peak), Wan 40×128 shape"
+PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
+KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_qk_amd", "csrc", "qknorm_rope.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, layout: str, style: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    key = "%s/%s/%s" % (workload, layout, style)
+    entry = rec.get("runs", {}).get(key)
+    return None if entry is None else entry.get("bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--layout", default="shared", choices=["shared", "per_head"])
+    ap.add_argument("--style", default=None, choices=[None, "interleaved", "rotate_half"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="budget for the CPU-oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def calib_copy(steps: int):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                      "copy_GBps": round(2 * n / dt / 1e9, 1), "steps": steps}))
+
+
+def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s):
+    """Time the fp64 oracle on the same workload: whole passes over every
+    token (Q and K), repeated until ``budget_s`` is spent; median pass time."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    bits = wl.u16(qkv_cpu)
+    H, D, T = w.heads, w.head_dim, w.tokens
+    chunk = 2048
+    out = np.empty((chunk, H, D), dtype=np.float64)
+    c_np, s_np = cos.numpy(), sin.numpy()
+    passes, spent = [], 0.0
+    while not passes or (spent < budget_s and len(passes) < 50):
+        t0 = time.perf_counter()
+        for a in range(0, T, chunk):
+            b = min(T, a + chunk)
+            for col0, g in ((0, qg), (H * D, kg)):
+                oracle.qknorm_rope(bits, "bf16", row_stride=3 * H * D, col0=col0, heads=H,
+                                   head_dim=D, gamma=g.numpy(), eps=wl.EPS, cos=c_np, sin=s_np,
+                                   style=style, t_begin=a, t_end=b, out=out[:b - a])
+        dt = time.perf_counter() - t0
+        passes.append(dt)
+        spent += dt
+    per_pass = float(np.median(passes))
+    nbytes = wl.algorithmic_bytes(T, H, D)
+    return {"value": round(nbytes / per_pass / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "ms_per_pass": round(per_pass * 1e3, 1),
+            "sample": "%d whole passes over all %d tokens x %d Q+K heads (median pass), fp64 "
+                      "C oracle with OpenMP, fp64 output in %d-token chunks"
+                      % (len(passes), T, 2 * H, chunk)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the pass needs no collective; "
+              "run with --gpus 1)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_qk_amd as qkr
+    import workloads as wl
+
+    if args.calib_copy:
+        calib_copy(max(1, args.steps))
+        return 0
+
+    qkr.load_library()
+    w = wl.WORKLOADS[args.workload]
+    style = args.style or w.styles[0]
+    H, D, T = w.heads, w.head_dim, w.tokens
+    assert w.layout == "fused", "bench times the fused QKV workloads"
+    dev = torch.device("cuda:0")
+
+    qkv_cpu = wl.fused_qkv(w.seed, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, style)
+    x = qkv_cpu.to(dev)
+    g1, g2 = qg.to(dev), kg.to(dev)
+    c, s = cos.to(dev), sin.to(dev)
+    if args.layout == "per_head":
+        c, s = wl.expand_per_head(c, H), wl.expand_per_head(s, H)
+    nbytes = wl.algorithmic_bytes(T, H, D, cos_layout=args.layout)
+
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+
+    def launch():
+        qkr.qknorm_rope_fused(x, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS,
+                              style=style, cos_layout=args.layout, stream=handle)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(K):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    region_ms = region0.elapsed_time(region1)
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3   # µs
+    mean_us = float(per.mean())
+    achieved = nbytes / (mean_us * 1e-6) / 1e9
+    value = nbytes * K / (region_ms * 1e-3) / 1e9
+    info = qkr.kernel_info(D, args.layout, qkr.binding.QKR_FP32, style, qkr.binding.QKR_BF16)
+
+    traffic = measured_traffic(args.workload, args.layout, style)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(region_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: fused QKV bf16 [%d, 3x%dx%d], %s RoPE, %s fp32 cos/sin"
+                               % (w.key, T, H, D, style, args.layout),
+                   "tokens": T, "heads": H, "head_dim": D, "layout": args.layout,
+                   "style": style, "math": "f32", "parallelism": "single GPU"},
+        "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
+                        "p10": round(float(np.percentile(per, 10)), 2),
+                        "p90": round(float(np.percentile(per, 90)), 2)},
+        "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
+        "bytes_per_call": nbytes,
+        "wall_s_timed": round(wall, 4),
+        "kernel": info,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style,
+                                              args.cpu_seconds)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

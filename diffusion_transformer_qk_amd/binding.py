@@ -1,0 +1,196 @@
+"""ctypes binding of ``libqknorm_rope.so`` (argument marshalling only).
+
+Every step of the pass runs in the HIP kernels behind the C ABI declared in
+``include/qknorm_rope.h``; this module turns torch tensors into device
+pointers, sizes and enum codes and raises on a non-zero status.  There is no
+fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqknorm_rope.so")
+
+QKR_OK = 0
+QKR_ERR_NULL, QKR_ERR_SHAPE, QKR_ERR_ALIGN = -1, -2, -3
+QKR_ERR_UNSUPPORTED, QKR_ERR_MODE, QKR_ERR_HIP, QKR_ERR_ARG = -4, -5, -6, -7
+QKR_BF16, QKR_FP16, QKR_FP32 = 0, 1, 2
+QKR_COS_SHARED, QKR_COS_PER_HEAD = 0, 1
+QKR_ROPE_INTERLEAVED, QKR_ROPE_ROTATE_HALF = 0, 1
+
+LAYOUTS = {"shared": QKR_COS_SHARED, "per_head": QKR_COS_PER_HEAD}
+STYLES = {"interleaved": QKR_ROPE_INTERLEAVED, "rotate_half": QKR_ROPE_ROTATE_HALF}
+EXPORTS = ("qknorm_rope_fused", "qknorm_rope_strerror", "qknorm_rope_version",
+           "qknorm_rope_kernel_info")
+
+
+class QkrError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("qknorm_rope: %s (status %d)" % (message, status))
+        self.status = status
+
+
+class KernelInfo(ctypes.Structure):
+    _fields_ = [("num_vgprs", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("scratch_bytes", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("tokens_per_block", ctypes.c_int32), ("heads_in_flight", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libqknorm_rope.so is not built (%s); run __graft_entry__.build() or "
+            "python -m diffusion_transformer_qk_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    lib.qknorm_rope_fused.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, f32, vp, vp,
+                                      i32, i32, i32, i32, vp]
+    lib.qknorm_rope_fused.restype = ctypes.c_int
+    lib.qknorm_rope_strerror.argtypes = [ctypes.c_int]
+    lib.qknorm_rope_strerror.restype = ctypes.c_char_p
+    lib.qknorm_rope_version.argtypes = []
+    lib.qknorm_rope_version.restype = ctypes.c_int
+    lib.qknorm_rope_kernel_info.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(KernelInfo)]
+    lib.qknorm_rope_kernel_info.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().qknorm_rope_strerror(status).decode()
+
+
+def version() -> int:
+    return int(load_library().qknorm_rope_version())
+
+
+def _check(status: int):
+    if status != QKR_OK:
+        raise QkrError(status, strerror(status))
+
+
+def qknorm_rope_fused_raw(qkv: int, q: int, k: int, tokens: int, heads: int, head_dim: int,
+                          q_gamma: int, k_gamma: int, eps: float, cos: int, sin: int,
+                          cos_layout: int, cos_dtype: int, style: int, dtype: int,
+                          stream: int) -> int:
+    """The C entry point with integer pointers; returns the raw status."""
+    lib = load_library()
+    return int(lib.qknorm_rope_fused(qkv or None, q or None, k or None, tokens, heads, head_dim,
+                                     q_gamma or None, k_gamma or None, eps, cos or None,
+                                     sin or None, cos_layout, cos_dtype, style, dtype,
+                                     stream or None))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _x_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return QKR_BF16
+    if t.dtype == torch.float16:
+        return QKR_FP16
+    raise ValueError("q/k/qkv must be bfloat16 or float16, got %s" % t.dtype)
+
+
+def _table_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return QKR_FP32
+    if t.dtype == torch.bfloat16:
+        return QKR_BF16
+    raise ValueError("cos/sin must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return t.data_ptr()
+
+
+def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
+                      cos=None, sin=None, eps: float = 1e-6, heads: int | None = None,
+                      head_dim: int | None = None, cos_layout: str = "shared",
+                      style: str = "interleaved", stream=None) -> None:
+    """Apply the fused QK-norm + RoPE in place (see ``include/qknorm_rope.h``).
+
+    Fused mode: ``qkv`` is [tokens, 3*heads*head_dim] (any leading shape whose
+    last dimension is 3*heads*head_dim); ``head_dim`` defaults to the gamma
+    length and ``heads`` to last_dim / (3*head_dim).
+    Separate mode: ``q`` and/or ``k`` are [..., heads, head_dim].
+    ``cos``/``sin``: [tokens, head_dim] ("shared") or [tokens, heads, head_dim]
+    ("per_head"), float32 or bfloat16.  ``stream``: a torch stream or a raw
+    hipStream_t integer; defaults to the current stream.
+    """
+    torch = _torch()
+    if qkv is not None:
+        ref = qkv
+        gam = q_gamma if q_gamma is not None else k_gamma
+        if head_dim is None:
+            if gam is None:
+                raise ValueError("head_dim is needed")
+            head_dim = gam.numel()
+        if heads is None:
+            heads = qkv.shape[-1] // (3 * head_dim)
+        if qkv.shape[-1] != 3 * heads * head_dim:
+            raise ValueError("qkv last dimension must be 3*heads*head_dim")
+        tokens = qkv.numel() // qkv.shape[-1] if qkv.numel() else 0
+    else:
+        ref = q if q is not None else k
+        if ref is None:
+            raise ValueError("pass qkv, or q and/or k")
+        if ref.dim() < 2:
+            raise ValueError("q/k must be [..., heads, head_dim]")
+        head_dim = ref.shape[-1] if head_dim is None else head_dim
+        heads = ref.shape[-2] if heads is None else heads
+        tokens = ref.numel() // (heads * head_dim) if ref.numel() else 0
+        if q is not None and k is not None and (q.shape != k.shape or q.dtype != k.dtype):
+            raise ValueError("q and k must have the same shape and dtype")
+    if cos is None or sin is None:
+        raise ValueError("cos and sin are required")
+    if cos.dtype != sin.dtype or cos.shape != sin.shape:
+        raise ValueError("cos and sin must match in shape and dtype")
+    rows = tokens * (heads if cos_layout == "per_head" else 1)
+    if cos.numel() != rows * head_dim:
+        raise ValueError("cos/sin hold %d values, expected %d for the %s layout"
+                         % (cos.numel(), rows * head_dim, cos_layout))
+    for g in (q_gamma, k_gamma):
+        if g is not None and (g.dtype != torch.float32 or g.numel() != head_dim):
+            raise ValueError("gamma must be float32 [head_dim]")
+    if stream is None:
+        stream_ptr = torch.cuda.current_stream(ref.device).cuda_stream if ref.is_cuda else 0
+    elif isinstance(stream, int):
+        stream_ptr = stream
+    else:
+        stream_ptr = stream.cuda_stream
+    status = qknorm_rope_fused_raw(
+        _ptr(qkv), _ptr(q), _ptr(k), tokens, heads, head_dim, _ptr(q_gamma), _ptr(k_gamma),
+        float(eps), _ptr(cos), _ptr(sin), LAYOUTS[cos_layout], _table_code(cos),
+        STYLES[style], _x_code(ref), stream_ptr)
+    _check(status)
+
+
+def kernel_info(head_dim: int = 128, cos_layout: str = "shared", cos_dtype: int = QKR_FP32,
+                style: str = "interleaved", dtype: int = QKR_BF16) -> dict:
+    """Registers, LDS and scratch of the kernel a configuration launches."""
+    info = KernelInfo()
+    _check(load_library().qknorm_rope_kernel_info(head_dim, LAYOUTS[cos_layout], cos_dtype,
+                                                  STYLES[style], dtype, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in KernelInfo._fields_}

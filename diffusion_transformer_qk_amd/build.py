@@ -1,0 +1,55 @@
+"""Compile the HIP library ``libqknorm_rope.so`` for gfx950 with hipcc.
+
+Usage:  python -m diffusion_transformer_qk_amd.build [--save-temps DIR]
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "qknorm_rope.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libqknorm_rope.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    "--offload-arch=" + ARCH,
+    "-O3", "-std=c++17", "-fPIC", "-shared",
+    # exact fp32 operation order: no implicit fma contraction, so both cos/sin
+    # layouts execute identical arithmetic
+    "-ffp-contract=off",
+    # no packed fp32 instructions on this target
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found")
+    return path
+
+
+def build(save_temps: str | None = None) -> str:
+    """Build the library in-tree and return its path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cwd = None
+    if save_temps:
+        os.makedirs(save_temps, exist_ok=True)
+        cmd.insert(1, "--save-temps")
+        cwd = save_temps
+    subprocess.run(cmd, check=True, cwd=cwd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--save-temps", default=None, help="keep ISA/IR in this directory")
+    print(build(ap.parse_args().save_temps))

@@ -1,0 +1,463 @@
+// qknorm_rope.hip -- fused diffusion-transformer QK-norm + RoPE for gfx950.
+//
+// The pass (TensorRT-LLM PR "VisualGen Wan: deduplicate shared RoPE SMEM
+// staging", Description; TensorRT-Model-Connect PR "perf(diffusion): fused
+// qknorm rope Flux 2.0", intro): per token and per Q/K head, RMSNorm over
+// head_dim with a learned weight, then RoPE with a cos/sin row indexed by
+// dimension, in place; V untouched.  Math in fp32, one RNE rounding at the end.
+//
+// Work mapping (memory-bound: no matrix cores):
+//   * a head of D elements is D/8 lanes, each holding 8 consecutive elements
+//     in one 16-byte access; a wave covers 64/(D/8) heads per iteration;
+//   * one wave owns one (token, tensor) slice: all H heads of Q, or of K, for
+//     one token, with U iterations of loads in flight before any math;
+//   * a 256-thread workgroup holds 4 waves = 2 tokens x {Q, K} (fused or two
+//     separate tensors) or 4 tokens of a single tensor;
+//   * shared layout: the workgroup stages each token's cos and sin rows once
+//     in LDS as fp32 and every head indexes them by dimension (the row is
+//     read from HBM once per token, not once per head);
+//   * per-lane rotation coefficients A = gamma*cos and B = +/-gamma_partner*sin
+//     are formed once per token (shared) or per head (per-head layout) with
+//     the same instructions, so both layouts give bit-identical output;
+//   * sum of squares: in-lane fma chain, then a DPP butterfly across the
+//     head's lanes (quad_perm xor1 / xor2, row_half_mirror, row_mirror) that
+//     leaves the identical sum in every lane of the head;
+//   * rotate-half partners sit D/2 elements away = half the head's lanes:
+//     exchanged with DPP row_ror:8 (D = 128) or ds_swizzle xor 4 (D = 64);
+//   * fp32 -> bf16/fp16 with the packed round-to-nearest-even converts.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "qknorm_rope.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr int kVec = 8;                 // 16-bit elements per 16-byte access
+constexpr int kInterleaved = QKR_ROPE_INTERLEAVED;
+constexpr int kRotateHalf = QKR_ROPE_ROTATE_HALF;
+constexpr int kUnrollShared = 8;        // head iterations in flight per lane (shared)
+constexpr int kUnrollPerHead = 4;       // (per-head layout also loads its cos/sin rows)
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct Params {
+    uint16_t* x[2];            // tensor s: element (t, h, d) at x[s] + t*row_stride + h*D + d
+    const float* gamma[2];     // weight of tensor s
+    const void* cos;
+    const void* sin;
+    int64_t row_stride;        // elements between consecutive tokens
+    int64_t tokens;
+    int32_t heads;
+    int32_t n_tensors;         // 1 or 2
+    float eps;
+};
+
+// ---------------------------------------------------------------- lane helpers
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the L lanes of one head (L = 8 or 16, aligned groups).  Each step
+// adds the same two partial sums in every lane, so all lanes end bit-equal.
+template <int L>
+__device__ __forceinline__ float head_sum(float v)
+{
+    v += dpp<0xB1>(v);       // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);       // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);      // row_half_mirror: the other quad of the 8-lane half
+    if constexpr (L == 16)
+        v += dpp<0x140>(v);  // row_mirror: the other half of the 16-lane row
+    return v;
+}
+
+// Value held by the lane L/2 positions away within the head (the lane whose
+// dimensions are D/2 away).
+template <int L>
+__device__ __forceinline__ float half_head_partner(float v)
+{
+    if constexpr (L == 16)
+        return dpp<0x128>(v);  // row_ror:8 == lane ^ 8 inside a 16-lane row
+    else
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                     0x101F));  // lane ^ 4
+}
+
+template <bool FP16>
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8])
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if constexpr (FP16) {
+            const f16x2 h = __builtin_bit_cast(f16x2, w[k]);
+            f[2 * k] = (float)h.x;
+            f[2 * k + 1] = (float)h.y;
+        } else {
+            f[2 * k] = __uint_as_float(w[k] << 16);
+            f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+}
+
+template <bool FP16>
+__device__ __forceinline__ uint4 pack8(const float o[8])
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x2 pr = {o[2 * k], o[2 * k + 1]};
+        if constexpr (FP16)
+            w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));
+        else
+            w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ void load_f32x8(const float* p, float f[8])
+{
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// Eight consecutive table entries starting at element `index`, widened to fp32.
+template <bool BF16_TABLE>
+__device__ __forceinline__ void load_table8(const void* table, int64_t index, float f[8])
+{
+    if constexpr (BF16_TABLE)
+        unpack8<false>(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(table) + index), f);
+    else
+        load_f32x8(static_cast<const float*>(table) + index, f);
+}
+
+// o[d] = n[d] c[d] + sign(d) n[partner(d)] s[d] with n = y * gamma, folded
+// into A[d] = gamma[d] c[d] and B[d] = sign(d) gamma[partner(d)] s[d].
+template <int D, int STYLE>
+__device__ __forceinline__ void rotation_coeffs(const float g[8], const float gp[8], const float c[8],
+                                                const float s[8], int d0, float A[8], float B[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        A[i] = g[i] * c[i];
+        const float b = gp[i] * s[i];
+        const bool first_of_pair = STYLE == kInterleaved ? (i % 2 == 0) : (d0 < D / 2);
+        B[i] = first_of_pair ? -b : b;
+    }
+}
+
+// One head's slice in this lane: 8 elements in, 8 rotated, normalised out.
+template <int D, int STYLE, bool X_FP16>
+__device__ __forceinline__ uint4 head_math(const uint4 v, const float A[8], const float B[8], float eps)
+{
+    constexpr int L = D / kVec;
+    float f[8];
+    unpack8<X_FP16>(v, f);
+    float ss = f[0] * f[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        ss = __builtin_fmaf(f[i], f[i], ss);
+    ss = head_sum<L>(ss);
+    const float r = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / D, eps));
+    float y[8], yp[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        y[i] = f[i] * r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        yp[i] = STYLE == kInterleaved ? y[i ^ 1] : half_head_partner<L>(y[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        o[i] = __builtin_fmaf(y[i], A[i], yp[i] * B[i]);
+    return pack8<X_FP16>(o);
+}
+
+// ---------------------------------------------------------------- the kernel
+
+template <int D, int STYLE, bool PER_HEAD, bool COS_BF16, bool X_FP16, int U>
+__global__ __launch_bounds__(kBlock) void qknorm_rope_kernel(const Params p)
+{
+    constexpr int L = D / kVec;       // lanes per head
+    constexpr int HPI = kWave / L;    // heads per wave iteration
+    __shared__ float stage[PER_HEAD ? 4 : kWavesPerBlock * 2 * D];   // [token][cos | sin][D]
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int two = p.n_tensors == 2 ? 1 : 0;
+    const int tokens_per_block = kWavesPerBlock >> two;
+    const int64_t t_first = (int64_t)blockIdx.x * tokens_per_block;
+    const int64_t t = t_first + (wave >> two);
+    const int s = wave & two;
+
+    if constexpr (!PER_HEAD) {
+        constexpr int per_chunk = COS_BF16 ? 8 : 4;      // table entries per 16-byte chunk
+        constexpr int chunks = D / per_chunk;            // chunks per table row
+        const int n_chunks = tokens_per_block * 2 * chunks;
+        for (int i = tid; i < n_chunks; i += kBlock) {
+            const int r = i / (2 * chunks);
+            const int tab = (i / chunks) & 1;
+            const int c = i % chunks;
+            const int64_t tt = t_first + r;
+            if (tt < p.tokens) {
+                float* dst = stage + (r * 2 + tab) * D + c * per_chunk;
+                const void* src = tab ? p.sin : p.cos;
+                if constexpr (COS_BF16) {
+                    float f[8];
+                    load_table8<true>(src, tt * D + c * per_chunk, f);
+                    reinterpret_cast<float4*>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+                    reinterpret_cast<float4*>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+                } else {
+                    *reinterpret_cast<float4*>(dst) =
+                        reinterpret_cast<const float4*>(static_cast<const float*>(src) + tt * D)[c];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (t >= p.tokens)
+        return;
+
+    const int d0 = (lane % L) * kVec;   // this lane's first dimension
+    const int hs = lane / L;            // head slot within a wave iteration
+    const float* gam = p.gamma[s];
+    float g[8], gp[8];
+    load_f32x8(gam + d0, g);
+    if constexpr (STYLE == kInterleaved) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            gp[i] = g[i ^ 1];
+    } else {
+        load_f32x8(gam + (d0 + D / 2) % D, gp);
+    }
+
+    float A[8], B[8];
+    if constexpr (!PER_HEAD) {
+        const float* row_cs = stage + (wave >> two) * 2 * D;
+        float c[8], sn[8];
+        load_f32x8(row_cs + d0, c);
+        load_f32x8(row_cs + D + d0, sn);
+        rotation_coeffs<D, STYLE>(g, gp, c, sn, d0, A, B);
+    }
+
+    uint16_t* const row = p.x[s] + t * p.row_stride;
+    const int H = p.heads;
+    for (int h0 = 0; h0 < H; h0 += HPI * U) {
+        uint4 v[U];
+        float tc[PER_HEAD ? U : 1][8], ts[PER_HEAD ? U : 1][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int h = h0 + u * HPI + hs;
+            if (h < H) {
+                v[u] = *reinterpret_cast<const uint4*>(row + h * D + d0);
+                if constexpr (PER_HEAD) {
+                    const int64_t idx = (t * H + h) * D + d0;
+                    load_table8<COS_BF16>(p.cos, idx, tc[u]);
+                    load_table8<COS_BF16>(p.sin, idx, ts[u]);
+                }
+            } else {
+                v[u] = make_uint4(0, 0, 0, 0);
+                if constexpr (PER_HEAD) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        tc[u][i] = ts[u][i] = 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int h = h0 + u * HPI + hs;
+            uint4 out;
+            if constexpr (PER_HEAD) {
+                float Ah[8], Bh[8];
+                rotation_coeffs<D, STYLE>(g, gp, tc[u], ts[u], d0, Ah, Bh);
+                out = head_math<D, STYLE, X_FP16>(v[u], Ah, Bh, p.eps);
+            } else {
+                out = head_math<D, STYLE, X_FP16>(v[u], A, B, p.eps);
+            }
+            if (h < H)
+                *reinterpret_cast<uint4*>(row + h * D + d0) = out;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+using KernelFn = void (*)(Params);
+
+template <int D, int STYLE, bool PH, bool CB, bool XF>
+KernelFn kernel_ptr()
+{
+    return qknorm_rope_kernel<D, STYLE, PH, CB, XF, PH ? kUnrollPerHead : kUnrollShared>;
+}
+
+template <int D, int STYLE, bool PH, bool CB>
+KernelFn select_x(bool xf) { return xf ? kernel_ptr<D, STYLE, PH, CB, true>() : kernel_ptr<D, STYLE, PH, CB, false>(); }
+
+template <int D, int STYLE, bool PH>
+KernelFn select_c(bool cb, bool xf) { return cb ? select_x<D, STYLE, PH, true>(xf) : select_x<D, STYLE, PH, false>(xf); }
+
+template <int D, int STYLE>
+KernelFn select_l(bool ph, bool cb, bool xf) { return ph ? select_c<D, STYLE, true>(cb, xf) : select_c<D, STYLE, false>(cb, xf); }
+
+template <int D>
+KernelFn select_s(int style, bool ph, bool cb, bool xf)
+{
+    return style == kRotateHalf ? select_l<D, kRotateHalf>(ph, cb, xf) : select_l<D, kInterleaved>(ph, cb, xf);
+}
+
+KernelFn select_kernel(int head_dim, int style, int cos_layout, int cos_dtype, int dtype)
+{
+    const bool ph = cos_layout == QKR_COS_PER_HEAD;
+    const bool cb = cos_dtype == QKR_BF16;
+    const bool xf = dtype == QKR_FP16;
+    return head_dim == 128 ? select_s<128>(style, ph, cb, xf) : select_s<64>(style, ph, cb, xf);
+}
+
+int check_config(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype, int32_t style, int32_t dtype)
+{
+    if (cos_layout != QKR_COS_SHARED && cos_layout != QKR_COS_PER_HEAD)
+        return QKR_ERR_ARG;
+    if (style != QKR_ROPE_INTERLEAVED && style != QKR_ROPE_ROTATE_HALF)
+        return QKR_ERR_ARG;
+    if (cos_dtype < QKR_BF16 || cos_dtype > QKR_FP32 || dtype < QKR_BF16 || dtype > QKR_FP32)
+        return QKR_ERR_ARG;
+    if (head_dim != 64 && head_dim != 128)
+        return QKR_ERR_UNSUPPORTED;
+    if (cos_dtype == QKR_FP16 || dtype == QKR_FP32)
+        return QKR_ERR_UNSUPPORTED;
+    return QKR_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, int32_t heads,
+                                 int32_t head_dim, const float* q_gamma, const float* k_gamma,
+                                 float eps, const void* cos, const void* sin, int32_t cos_layout,
+                                 int32_t cos_dtype, int32_t style, int32_t dtype, void* stream)
+{
+    const int cfg = check_config(head_dim, cos_layout, cos_dtype, style, dtype);
+    if (cfg != QKR_OK)
+        return cfg;
+    if (!(eps > 0.0f) || !isfinite(eps))
+        return QKR_ERR_ARG;
+    if (tokens < 0 || tokens >= QKR_MAX_TOKENS || heads < 1 || heads > QKR_MAX_HEADS)
+        return QKR_ERR_SHAPE;
+    if (tokens == 0)
+        return QKR_OK;
+
+    Params p = {};
+    const int64_t hd = (int64_t)heads * head_dim;
+    if (qkv) {
+        if (q || k)
+            return QKR_ERR_MODE;
+        if (!q_gamma || !k_gamma)
+            return QKR_ERR_NULL;
+        uint16_t* base = static_cast<uint16_t*>(qkv);
+        p.x[0] = base;
+        p.x[1] = base + hd;
+        p.gamma[0] = q_gamma;
+        p.gamma[1] = k_gamma;
+        p.n_tensors = 2;
+        p.row_stride = 3 * hd;
+        if (!aligned16(qkv))
+            return QKR_ERR_ALIGN;
+    } else {
+        if (!q && !k)
+            return QKR_ERR_MODE;
+        int n = 0;
+        if (q) {
+            if (!q_gamma)
+                return QKR_ERR_NULL;
+            if (!aligned16(q))
+                return QKR_ERR_ALIGN;
+            p.x[n] = static_cast<uint16_t*>(q);
+            p.gamma[n++] = q_gamma;
+        }
+        if (k) {
+            if (!k_gamma)
+                return QKR_ERR_NULL;
+            if (!aligned16(k))
+                return QKR_ERR_ALIGN;
+            p.x[n] = static_cast<uint16_t*>(k);
+            p.gamma[n++] = k_gamma;
+        }
+        p.n_tensors = n;
+        p.row_stride = hd;
+    }
+    if (!cos || !sin)
+        return QKR_ERR_NULL;
+    if (!aligned16(cos) || !aligned16(sin))
+        return QKR_ERR_ALIGN;
+    for (int s = 0; s < p.n_tensors; ++s)
+        if (!aligned16(p.gamma[s]))
+            return QKR_ERR_ALIGN;
+
+    p.cos = cos;
+    p.sin = sin;
+    p.tokens = tokens;
+    p.heads = heads;
+    p.eps = eps;
+
+    const int tokens_per_block = kWavesPerBlock / p.n_tensors;
+    const int64_t blocks = (tokens + tokens_per_block - 1) / tokens_per_block;
+    KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype);
+    void* args[] = {&p};
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)blocks),
+                                     dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return QKR_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? QKR_OK : QKR_ERR_HIP;
+}
+
+extern "C" const char* qknorm_rope_strerror(int status)
+{
+    switch (status) {
+    case QKR_OK: return "ok";
+    case QKR_ERR_NULL: return "a required pointer is NULL";
+    case QKR_ERR_SHAPE: return "tokens or heads out of range";
+    case QKR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QKR_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case QKR_ERR_MODE: return "pass either qkv, or q and/or k (not both, not neither)";
+    case QKR_ERR_HIP: return "HIP launch or query failed";
+    case QKR_ERR_ARG: return "eps must be finite and > 0; enum argument out of range";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int qknorm_rope_version(void) { return QKNORM_ROPE_VERSION; }
+
+extern "C" int qknorm_rope_kernel_info(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype,
+                                       int32_t style, int32_t dtype, qkr_kernel_info* out)
+{
+    if (!out)
+        return QKR_ERR_NULL;
+    const int cfg = check_config(head_dim, cos_layout, cos_dtype, style, dtype);
+    if (cfg != QKR_OK)
+        return cfg;
+    hipFuncAttributes attr;
+    KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype);
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn)) != hipSuccess)
+        return QKR_ERR_HIP;
+    out->num_vgprs = attr.numRegs;
+    out->lds_bytes = (int32_t)attr.sharedSizeBytes;
+    out->scratch_bytes = (int32_t)attr.localSizeBytes;
+    out->block_threads = kBlock;
+    out->tokens_per_block = kWavesPerBlock / 2;
+    out->heads_in_flight = cos_layout == QKR_COS_PER_HEAD ? kUnrollPerHead : kUnrollShared;
+    return QKR_OK;
+}

@@ -1,0 +1,123 @@
+/*
+ * qknorm_rope.h -- C ABI of the fused diffusion-transformer QK-norm + RoPE
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (TensorRT-LLM PR "VisualGen Wan: deduplicate shared RoPE SMEM
+ * staging", Description; TensorRT-Model-Connect PR "perf(diffusion): fused
+ * qknorm rope Flux 2.0", intro): for every token and every Q and K head,
+ *
+ *   r      = 1 / sqrt(mean_d x[d]^2 + eps)          per-head RMSNorm over head_dim
+ *   n[d]   = x[d] * r * gamma[d]                     gamma: q_gamma for Q, k_gamma for K
+ *   o[a]   = n[a] * cos[a] - n[b] * sin[a]           for each rotary pair (a, b):
+ *   o[b]   = n[b] * cos[b] + n[a] * sin[b]             interleaved (2i, 2i+1) or
+ *                                                      rotate-half (i, i + head_dim/2)
+ *
+ * written back in place over Q and K, rounded once (round to nearest even) to
+ * the tensor's dtype; math is fp32 inside.  The cos/sin row of token t is
+ * either shared by all heads ([tokens, head_dim], "shared") or given per head
+ * ([tokens, heads, head_dim], "per-head"); row (t, h) serves Q head h and K
+ * head h.  The V slice of a fused buffer is never read or written.
+ *
+ * All pointers are DEVICE pointers owned by the caller; the library never
+ * allocates, frees or synchronises and keeps no state between calls (calls
+ * are thread-safe).  Q and K are modified in place; every other buffer is
+ * read-only.  Buffers must stay valid until the work queued on `stream`
+ * completes.  Work is only enqueued: the call returns before it runs.
+ */
+#ifndef QKNORM_ROPE_H
+#define QKNORM_ROPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QKNORM_ROPE_VERSION 1
+
+/* Return codes.  On any error nothing is enqueued and no buffer is touched. */
+enum {
+    QKR_OK = 0,
+    QKR_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    QKR_ERR_SHAPE = -2,       /* tokens < 0, heads < 1, or a size over the limits    */
+    QKR_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                    */
+    QKR_ERR_UNSUPPORTED = -4, /* head_dim not 64/128, or an unsupported dtype        */
+    QKR_ERR_MODE = -5,        /* not exactly one of {qkv} / {q and/or k}             */
+    QKR_ERR_HIP = -6,         /* the kernel launch (or an attribute query) failed     */
+    QKR_ERR_ARG = -7          /* eps not finite and > 0, or an enum out of range      */
+};
+
+/* Element types. */
+enum { QKR_BF16 = 0, QKR_FP16 = 1, QKR_FP32 = 2 };
+/* cos/sin layouts. */
+enum { QKR_COS_SHARED = 0, QKR_COS_PER_HEAD = 1 };
+/* RoPE pairing styles. */
+enum { QKR_ROPE_INTERLEAVED = 0, QKR_ROPE_ROTATE_HALF = 1 };
+
+/* Limits checked by qknorm_rope_fused. */
+#define QKR_MAX_TOKENS ((int64_t)1 << 31)   /* tokens must be below this     */
+#define QKR_MAX_HEADS 65536                 /* heads must not exceed this    */
+
+/*
+ * qknorm_rope_fused -- the pass, in place, on one stream.
+ *
+ * Modes (exactly one):
+ *   fused:    qkv != NULL, q == k == NULL.  qkv is [tokens, 3*heads*head_dim],
+ *             row-major, Q columns [0, H*D), K [H*D, 2*H*D), V [2*H*D, 3*H*D)
+ *             (V untouched).  q_gamma and k_gamma are both required.
+ *   separate: qkv == NULL and at least one of q, k != NULL.  Each given
+ *             tensor is [tokens, heads, head_dim] contiguous; a tensor that is
+ *             NULL is skipped and its gamma may be NULL.
+ *
+ * tokens      number of rows (batch folded in); 0 is a no-op that returns
+ *             QKR_OK once the scalar arguments are valid (pointers unchecked).
+ * heads       heads per tensor (Q, K and V have the same count), 1..65536.
+ * head_dim    64 or 128.
+ * q_gamma, k_gamma  fp32 [head_dim] norm weights.
+ * eps         added to the mean square inside the root; finite and > 0.
+ * cos, sin    cos_dtype (QKR_FP32 or QKR_BF16) tables, contiguous:
+ *             QKR_COS_SHARED [tokens, head_dim] or QKR_COS_PER_HEAD
+ *             [tokens, heads, head_dim]; indexed by dimension (no assumption
+ *             that paired dimensions hold equal values).
+ * style       QKR_ROPE_INTERLEAVED or QKR_ROPE_ROTATE_HALF.
+ * dtype       QKR_BF16 or QKR_FP16: element type of qkv / q / k.
+ * stream      a hipStream_t (NULL = the default stream).
+ *
+ * Every data pointer must be 16-byte aligned.  Returns QKR_OK or a negative
+ * QKR_ERR_* code; all checks happen before any HIP call.
+ */
+int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, int32_t heads,
+                      int32_t head_dim, const float* q_gamma, const float* k_gamma, float eps,
+                      const void* cos, const void* sin, int32_t cos_layout, int32_t cos_dtype,
+                      int32_t style, int32_t dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* qknorm_rope_strerror(int status);
+
+/* QKNORM_ROPE_VERSION of the built library. */
+int qknorm_rope_version(void);
+
+/* Resources of the kernel one configuration launches (from the code object). */
+typedef struct {
+    int32_t num_vgprs;        /* registers per lane                               */
+    int32_t lds_bytes;        /* static LDS per workgroup                         */
+    int32_t scratch_bytes;    /* private (spill) memory per lane; 0 expected       */
+    int32_t block_threads;    /* workgroup size the library launches              */
+    int32_t tokens_per_block; /* tokens one workgroup covers (fused mode)         */
+    int32_t heads_in_flight;  /* head loads each lane keeps in flight              */
+} qkr_kernel_info;
+
+/*
+ * qknorm_rope_kernel_info -- fill *out for the kernel that qknorm_rope_fused
+ * would launch for (head_dim, cos_layout, cos_dtype, style, dtype).  Needs a
+ * HIP device (queries the loaded code object).  Returns QKR_OK, QKR_ERR_NULL,
+ * QKR_ERR_ARG / QKR_ERR_UNSUPPORTED for a bad configuration, or QKR_ERR_HIP.
+ */
+int qknorm_rope_kernel_info(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype,
+                            int32_t style, int32_t dtype, qkr_kernel_info* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QKNORM_ROPE_H */

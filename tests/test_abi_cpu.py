@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: exports and argument validation.
+
+Every call here is rejected (or is the tokens == 0 no-op) before the library
+makes any HIP call, so nothing is launched.  Pointers are fake, aligned or
+misaligned integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_qk_amd as qkr
+from diffusion_transformer_qk_amd import binding as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "qknorm_rope.h")
+
+A = 0x10000          # a 16-byte aligned fake device address
+MIS = 0x10008        # 8-byte aligned only
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return set(re.findall(r"\b(qknorm_rope_\w+)\s*\(", text))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(qkr.LIB_PATH)
+    names = declared_functions()
+    assert names == set(b.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert qkr.version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert qkr.strerror(code) != "unknown status"
+    assert qkr.strerror(12345) == "unknown status"
+
+
+def call(**over):
+    args = dict(qkv=A, q=0, k=0, tokens=16, heads=40, head_dim=128, q_gamma=A, k_gamma=A,
+                eps=1e-6, cos=A, sin=A, cos_layout=0, cos_dtype=b.QKR_FP32, style=0,
+                dtype=b.QKR_BF16, stream=0)
+    args.update(over)
+    return qkr.qknorm_rope_fused_raw(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=96), b.QKR_ERR_UNSUPPORTED),
+    (dict(head_dim=256), b.QKR_ERR_UNSUPPORTED),
+    (dict(dtype=b.QKR_FP32), b.QKR_ERR_UNSUPPORTED),
+    (dict(cos_dtype=b.QKR_FP16), b.QKR_ERR_UNSUPPORTED),
+    (dict(dtype=7), b.QKR_ERR_ARG),
+    (dict(cos_dtype=-1), b.QKR_ERR_ARG),
+    (dict(style=2), b.QKR_ERR_ARG),
+    (dict(cos_layout=5), b.QKR_ERR_ARG),
+    (dict(eps=0.0), b.QKR_ERR_ARG),
+    (dict(eps=-1e-6), b.QKR_ERR_ARG),
+    (dict(eps=float("nan")), b.QKR_ERR_ARG),
+    (dict(eps=float("inf")), b.QKR_ERR_ARG),
+    (dict(tokens=-1), b.QKR_ERR_SHAPE),
+    (dict(tokens=1 << 31), b.QKR_ERR_SHAPE),
+    (dict(heads=0), b.QKR_ERR_SHAPE),
+    (dict(heads=65537), b.QKR_ERR_SHAPE),
+    (dict(qkv=A, q=A), b.QKR_ERR_MODE),
+    (dict(qkv=A, k=A), b.QKR_ERR_MODE),
+    (dict(qkv=0), b.QKR_ERR_MODE),
+    (dict(k_gamma=0), b.QKR_ERR_NULL),
+    (dict(q_gamma=0), b.QKR_ERR_NULL),
+    (dict(qkv=0, q=A, q_gamma=0), b.QKR_ERR_NULL),
+    (dict(qkv=0, k=A, k_gamma=0), b.QKR_ERR_NULL),
+    (dict(cos=0), b.QKR_ERR_NULL),
+    (dict(sin=0), b.QKR_ERR_NULL),
+    (dict(qkv=MIS), b.QKR_ERR_ALIGN),
+    (dict(qkv=0, q=MIS), b.QKR_ERR_ALIGN),
+    (dict(qkv=0, q=A, k=MIS), b.QKR_ERR_ALIGN),
+    (dict(cos=MIS), b.QKR_ERR_ALIGN),
+    (dict(sin=A + 4), b.QKR_ERR_ALIGN),
+    (dict(q_gamma=A + 4), b.QKR_ERR_ALIGN),
+    (dict(qkv=0, k=A, k_gamma=A + 12), b.QKR_ERR_ALIGN),
+])
+def test_rejects_before_any_hip_call(over, code):
+    assert call(**over) == code
+
+
+def test_zero_tokens_is_a_no_op():
+    # valid scalars: OK without looking at (or launching on) the pointers
+    assert call(tokens=0, qkv=0, q_gamma=0, k_gamma=0, cos=0, sin=0) == b.QKR_OK
+    # invalid scalars are still reported
+    assert call(tokens=0, head_dim=32) == b.QKR_ERR_UNSUPPORTED
+
+
+def test_separate_mode_skips_missing_tensor_gamma():
+    # k absent: its gamma may be NULL; the call is then only rejected for the table
+    assert call(qkv=0, q=A, k=0, k_gamma=0, cos=0) == b.QKR_ERR_NULL
+    assert call(qkv=0, q=A, k=0, k_gamma=0, cos=MIS) == b.QKR_ERR_ALIGN
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 3 * 2 * 64, dtype=torch.bfloat16)
+    g = torch.ones(64)
+    c = torch.ones(4, 64)
+    with pytest.raises(ValueError):
+        qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c)
+    with pytest.raises(ValueError):   # wrong table size
+        qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c[:3], sin=c[:3])

@@ -1,0 +1,434 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: max |gpu - oracle| <= 1.6e-2 for bf16 outputs and <= 2e-3 for fp16,
+comparing the decoded GPU output with the UNROUNDED fp64 oracle; on top of
+that the GPU output must equal the oracle's round-to-nearest-even image on all
+but a tiny fraction of elements (those where fp32 rounding sits at a rounding
+midpoint), and never by more than one unit in the last place.  Shared and
+per-head cos/sin layouts must agree bit for bit, V and every read-only input
+must stay bit-identical, and nothing outside the tensors may be written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_qk_amd as qkr
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1.6e-2, "fp16": 2e-3}
+MISMATCH_FRAC = {"bf16": 1e-3, "fp16": 2e-3}
+DEV = torch.device("cuda:0")
+PAD = 4096          # canary elements on each side of a tensor
+CANARY = 0x7E5A
+
+
+def _decode(t: torch.Tensor, dtype: str) -> np.ndarray:
+    bits = wl.u16(t.cpu())
+    if dtype == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    p, emin = (11, -14) if dtype == "fp16" else (8, -126)
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
+    return 2.0 ** (e - p + 1)
+
+
+FP32_NOISE = 8e-6   # fp32 math error, relative to the largest |o| of the head
+
+
+def rounding_bound(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-element error model: round to nearest (half an ulp of the exact
+    value) plus fp32 arithmetic noise.  The noise term scales with the head's
+    largest |o| because the two products of a rotated pair can cancel, leaving
+    a tiny output with an absolute fp32 error of the terms' size."""
+    scale = np.max(np.abs(ref), axis=-1, keepdims=True)
+    return 0.5 * _ulp(ref, dtype) + FP32_NOISE * scale
+
+
+def check_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> float:
+    """Assert the tolerance, the rounding model and the RNE agreement; return max_abs."""
+    got = got.reshape(ref.shape)
+    err = np.abs(got - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    assert max_abs <= TOL[dtype], "%s max_abs %.4g > %g (max|o| %.3g)" % (
+        what, max_abs, TOL[dtype], np.abs(ref).max())
+    over = err > rounding_bound(ref, dtype)
+    assert not over.any(), "%s: %d elements outside the rounding model, worst %.3g" % (
+        what, int(over.sum()), float((err - rounding_bound(ref, dtype)).max()))
+    rne = oracle.round_to(ref, dtype)
+    n_diff = int(np.count_nonzero(got != rne))
+    assert n_diff <= max(2, MISMATCH_FRAC[dtype] * got.size), "%s: %d of %d differ from RNE" % (
+        what, n_diff, got.size)
+    return max_abs
+
+
+def check_rounding_bound(got: np.ndarray, ref: np.ndarray, dtype: str, what=""):
+    """For inputs whose outputs may exceed |o| = 8 (beyond the fixed tolerance)."""
+    got = got.reshape(ref.shape)
+    assert np.all(np.abs(got - ref) <= rounding_bound(ref, dtype)), what
+
+
+def guarded(t_cpu: torch.Tensor):
+    """Device copy of t inside a canary-filled buffer: (view, whole buffer)."""
+    n = t_cpu.numel()
+    buf = torch.full((n + 2 * PAD,), CANARY, dtype=torch.int16, device=DEV)
+    view = buf[PAD:PAD + n].view(t_cpu.dtype).view(t_cpu.shape)
+    view.copy_(t_cpu.to(DEV))
+    return view, buf
+
+
+def canaries_intact(buf: torch.Tensor) -> bool:
+    return bool((buf[:PAD] == CANARY).all()) and bool((buf[-PAD:] == CANARY).all())
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def tables(pos, split, d, style, dtype="fp32"):
+    return wl.rope_tables(pos, split, d, style, dtype=dtype)
+
+
+def table_np(t: torch.Tensor):
+    return t.numpy() if t.dtype == torch.float32 else wl.u16(t)
+
+
+def cos_dtype_name(t: torch.Tensor) -> str:
+    return "fp32" if t.dtype == torch.float32 else "bf16"
+
+
+def run_fused(qkv_cpu, qg, kg, cos, sin, style, layout="shared", eps=wl.EPS, stream=None):
+    """Run the pass on a guarded device copy; check canaries; return CPU output."""
+    x, buf = guarded(qkv_cpu)
+    g = (dev(qg), dev(kg))
+    c, s = dev(cos), dev(sin)
+    keep = [t.clone() for t in (*g, c, s)]
+    qkr.qknorm_rope_fused(x, q_gamma=g[0], k_gamma=g[1], cos=c, sin=s, eps=eps, style=style,
+                          cos_layout=layout, stream=stream)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf), "write outside the QKV buffer"
+    for a, b in zip(keep, (*g, c, s)):
+        assert torch.equal(a, b), "a read-only input changed"
+    return x.cpu()
+
+
+def oracle_fused(qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout="shared",
+                 t_begin=0, t_end=None):
+    return oracle.fused_qk(wl.u16(qkv_cpu), x_dtype, heads=H, head_dim=D, q_gamma=qg.numpy(),
+                           k_gamma=kg.numpy(), eps=wl.EPS, cos=table_np(cos), sin=table_np(sin),
+                           cos_dtype=cos_dtype_name(cos), cos_layout=layout, style=style,
+                           t_begin=t_begin, t_end=t_end)
+
+
+def assert_v_untouched(out, inp, H, D):
+    a = out.view(torch.int16).reshape(out.shape[0], -1)[:, 2 * H * D:]
+    b = inp.view(torch.int16).reshape(inp.shape[0], -1)[:, 2 * H * D:]
+    assert torch.equal(a, b), "V slice changed"
+
+
+def compare_fused(out, qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout="shared",
+                  what=""):
+    T = qkv_cpu.shape[0]
+    q_ref, k_ref = oracle_fused(qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout)
+    got = _decode(out, x_dtype).reshape(T, 3, H, D)
+    m1 = check_close(got[:, 0], q_ref, x_dtype, what + " Q")
+    m2 = check_close(got[:, 1], k_ref, x_dtype, what + " K")
+    assert_v_untouched(out, qkv_cpu, H, D)
+    return max(m1, m2)
+
+
+# ----------------------------------------------------------------------------- kernel resources
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("layout", ["shared", "per_head"])
+def test_kernels_do_not_spill(head_dim, layout):
+    for style in ("interleaved", "rotate_half"):
+        for cd in (qkr.binding.QKR_FP32, qkr.binding.QKR_BF16):
+            for xd in (qkr.binding.QKR_BF16, qkr.binding.QKR_FP16):
+                info = qkr.kernel_info(head_dim, layout, cd, style, xd)
+                assert info["scratch_bytes"] == 0, info
+                assert 0 < info["num_vgprs"] <= 128, info
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+
+def test_tiny_workload():
+    w = wl.WORKLOADS["tiny"]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, "interleaved")
+    out = run_fused(qkv, qg, kg, cos, sin, "interleaved")
+    m = compare_fused(out, qkv, "bf16", H, D, qg, kg, cos, sin, "interleaved", what="tiny")
+    print("tiny max_abs", m)
+
+
+def test_mid_workload_and_layout_parity():
+    w = wl.WORKLOADS["mid"]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, "rotate_half")
+    shared = run_fused(qkv, qg, kg, cos, sin, "rotate_half")
+    compare_fused(shared, qkv, "bf16", H, D, qg, kg, cos, sin, "rotate_half", what="mid")
+    per_head = run_fused(qkv, qg, kg, wl.expand_per_head(cos, H), wl.expand_per_head(sin, H),
+                         "rotate_half", layout="per_head")
+    assert torch.equal(shared.view(torch.int16), per_head.view(torch.int16))
+
+
+@pytest.mark.parametrize("x_dtype", ["fp16", "bf16"])
+def test_flux_workload_separate_q_k(x_dtype):
+    w = wl.WORKLOADS["flux"]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    q, k = wl.separate_qk(w.seed, T, H, D, (x_dtype,))[x_dtype]
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, "interleaved")
+    qd, qbuf = guarded(q)
+    kd, kbuf = guarded(k)
+    qkr.qknorm_rope_fused(q=qd, k=kd, q_gamma=dev(qg), k_gamma=dev(kg), cos=dev(cos),
+                          sin=dev(sin), eps=wl.EPS, style="interleaved")
+    torch.cuda.synchronize()
+    assert canaries_intact(qbuf) and canaries_intact(kbuf)
+    kw = dict(row_stride=H * D, col0=0, heads=H, head_dim=D, eps=wl.EPS, cos=cos.numpy(),
+              sin=sin.numpy(), style="interleaved")
+    q_ref = oracle.qknorm_rope(wl.u16(q), x_dtype, gamma=qg.numpy(), **kw)
+    k_ref = oracle.qknorm_rope(wl.u16(k), x_dtype, gamma=kg.numpy(), **kw)
+    mq = check_close(_decode(qd, x_dtype), q_ref, x_dtype, "flux q")
+    mk = check_close(_decode(kd, x_dtype), k_ref, x_dtype, "flux k")
+    # text tokens sit at position 0: their output is the norm alone
+    print("flux", x_dtype, "max_abs", mq, mk)
+
+
+def _sample_windows(T, rng, n=12, width=48):
+    starts = sorted(set(rng.integers(0, T - width, n).tolist()))
+    wins = [(0, width)] + [(s, s + width) for s in starts] + [(T - width - 3, T)]
+    return wins
+
+
+def _check_sampled(out, qkv, H, D, qg, kg, cos, sin, style, seed, what):
+    T = qkv.shape[0]
+    rng = np.random.default_rng(seed)
+    got_all = out.view(T, 3, H, D)
+    worst = 0.0
+    for a, b in _sample_windows(T, rng):
+        q_ref, k_ref = oracle_fused(qkv, "bf16", H, D, qg, kg, cos, sin, style, t_begin=a, t_end=b)
+        got = _decode(got_all[a:b].contiguous(), "bf16").reshape(b - a, 3, H, D)
+        worst = max(worst, check_close(got[:, 0], q_ref, "bf16", "%s Q[%d:%d]" % (what, a, b)),
+                    check_close(got[:, 1], k_ref, "bf16", "%s K[%d:%d]" % (what, a, b)))
+    return worst
+
+
+def test_headline_workload_sampled():
+    """32760 x 3*40*128 bf16, the launch the bench times; oracle on sampled windows."""
+    w = wl.WORKLOADS["headline"]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, "interleaved")
+    out = run_fused(qkv, qg, kg, cos, sin, "interleaved")
+    assert_v_untouched(out, qkv, H, D)
+    m = _check_sampled(out, qkv, H, D, qg, kg, cos, sin, "interleaved", 99, "headline")
+    print("headline sampled max_abs", m)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("style", ["interleaved", "rotate_half"])
+def test_large_workload_sampled_and_layout_parity(style):
+    w = wl.WORKLOADS["large"]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, style)
+    x_in = dev(qkv)
+    g = (dev(qg), dev(kg))
+    c, s = dev(cos), dev(sin)
+    a = x_in.clone()
+    qkr.qknorm_rope_fused(a, q_gamma=g[0], k_gamma=g[1], cos=c, sin=s, style=style)
+    cph, sph = wl.expand_per_head(c, H), wl.expand_per_head(s, H)
+    b = x_in.clone()
+    qkr.qknorm_rope_fused(b, q_gamma=g[0], k_gamma=g[1], cos=cph, sin=sph, style=style,
+                          cos_layout="per_head")
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "layouts differ"
+    del b, cph, sph
+    out = a.cpu()
+    assert_v_untouched(out, qkv, H, D)
+    m = _check_sampled(out, qkv, H, D, qg, kg, cos, sin, style, 7, "large " + style)
+    print("large", style, "sampled max_abs", m)
+
+
+# ----------------------------------------------------------------------------- exact layout parity
+
+
+@pytest.mark.parametrize("style", ["interleaved", "rotate_half"])
+@pytest.mark.parametrize("heads,head_dim", [(24, 64), (24, 128), (40, 128)])
+def test_shared_row_matches_expanded_bitwise(style, heads, head_dim):
+    """Shared fp32 row vs the same row materialised per head: rtol = atol = 0."""
+    T = 256
+    qkv = wl.fused_qkv(2000 + heads + head_dim, T, heads, head_dim, "bf16")
+    qg, kg = wl.norm_weights(2000 + heads, head_dim)
+    cos, sin = tables(np.arange(T) * 5, (head_dim // 2,), head_dim, style)
+    a = run_fused(qkv, qg, kg, cos, sin, style)
+    b = run_fused(qkv, qg, kg, wl.expand_per_head(cos, heads), wl.expand_per_head(sin, heads),
+                  style, layout="per_head")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_v_untouched(a, qkv, heads, head_dim)
+    compare_fused(a, qkv, "bf16", heads, head_dim, qg, kg, cos, sin, style, what="parity")
+
+
+@pytest.mark.parametrize("style", ["interleaved", "rotate_half"])
+def test_bf16_tables_shared_vs_per_head(style):
+    T, H, D = 133, 6, 128
+    qkv = wl.fused_qkv(31, T, H, D, "fp16")
+    qg, kg = wl.norm_weights(31, D)
+    cos, sin = tables(np.arange(T), (D // 2,), D, style, dtype="bf16")
+    a = run_fused(qkv, qg, kg, cos, sin, style)
+    b = run_fused(qkv, qg, kg, wl.expand_per_head(cos, H), wl.expand_per_head(sin, H), style,
+                  layout="per_head")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    compare_fused(a, qkv, "fp16", H, D, qg, kg, cos, sin, style, what="bf16 tables")
+
+
+def test_per_head_distinct_rows():
+    """Per-head rows that are NOT a broadcast: row (t, h) must be used for head h."""
+    T, H, D = 37, 5, 64
+    rng = np.random.default_rng(5)
+    qkv = wl.fused_qkv(32, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(32, D)
+    ang = rng.uniform(0, 6.3, (T, H, D // 2))
+    cos = torch.from_numpy(np.repeat(np.cos(ang), 2, axis=-1).astype(np.float32))
+    sin = torch.from_numpy(np.repeat(np.sin(ang), 2, axis=-1).astype(np.float32))
+    out = run_fused(qkv, qg, kg, cos, sin, "interleaved", layout="per_head")
+    compare_fused(out, qkv, "bf16", H, D, qg, kg, cos, sin, "interleaved", layout="per_head",
+                  what="per-head rows")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize("T,H,D", [(1, 1, 64), (1, 40, 128), (3, 5, 128), (5, 3, 64),
+                                   (257, 7, 128), (130, 33, 64), (2, 9, 128), (65, 17, 64)])
+@pytest.mark.parametrize("style", ["interleaved", "rotate_half"])
+def test_ragged_shapes(T, H, D, style):
+    qkv = wl.fused_qkv(40 + T + H, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(41, D)
+    cos, sin = tables(np.arange(T) * 11, (D // 2,), D, style)
+    out = run_fused(qkv, qg, kg, cos, sin, style)
+    compare_fused(out, qkv, "bf16", H, D, qg, kg, cos, sin, style, what="ragged")
+
+
+@pytest.mark.parametrize("which", ["q", "k", "both"])
+@pytest.mark.parametrize("T", [1, 6, 77])
+def test_separate_single_tensor(which, T):
+    H, D = 6, 128
+    q, k = wl.separate_qk(50 + T, T, H, D, ("fp16",))["fp16"]
+    qg, kg = wl.norm_weights(51, D)
+    cos, sin = tables(np.arange(T), (D // 2,), D, "rotate_half")
+    qd, qbuf = guarded(q)
+    kd, kbuf = guarded(k)
+    args = dict(cos=dev(cos), sin=dev(sin), style="rotate_half")
+    if which in ("q", "both"):
+        args.update(q=qd, q_gamma=dev(qg))
+    if which in ("k", "both"):
+        args.update(k=kd, k_gamma=dev(kg))
+    qkr.qknorm_rope_fused(**args)
+    torch.cuda.synchronize()
+    assert canaries_intact(qbuf) and canaries_intact(kbuf)
+    kw = dict(row_stride=H * D, col0=0, heads=H, head_dim=D, eps=wl.EPS, cos=cos.numpy(),
+              sin=sin.numpy(), style="rotate_half")
+    for name, t_in, t_dev, g in (("q", q, qd, qg), ("k", k, kd, kg)):
+        if which in (name, "both"):
+            ref = oracle.qknorm_rope(wl.u16(t_in), "fp16", gamma=g.numpy(), **kw)
+            check_close(_decode(t_dev, "fp16"), ref, "fp16", name)
+        else:
+            assert torch.equal(t_dev.cpu().view(torch.int16), t_in.view(torch.int16))
+
+
+def test_zero_tokens_changes_nothing():
+    x = torch.zeros(0, 3 * 4 * 64, dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(64, device=DEV)
+    c = torch.ones(0, 64, device=DEV)
+    qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c)
+    torch.cuda.synchronize()
+
+
+def test_max_heads():
+    T, H, D = 2, 65536, 64
+    qkv = wl.fused_qkv(60, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(60, D)
+    cos, sin = tables(np.arange(T), (D // 2,), D, "interleaved")
+    out = run_fused(qkv, qg, kg, cos, sin, "interleaved")
+    compare_fused(out, qkv, "bf16", H, D, qg, kg, cos, sin, "interleaved", what="max heads")
+
+
+def test_zero_heads_and_extreme_magnitudes():
+    T, H, D = 9, 4, 128
+    rng = np.random.default_rng(70)
+    raw = rng.standard_normal((T, 3 * H * D)).astype(np.float32)
+    raw[0, :H * D] = 0                      # every Q head of token 0 is zero
+    raw[1, H * D:2 * H * D] = -0.0          # every K head of token 1 is -0
+    raw[2] *= 8e3                           # large magnitudes (|x| < 65504 in fp16)
+    raw[3] *= 1e-3
+    raw[4, 5] = 900.0                       # one spike: |o| of that head reaches ~11
+    for x_dtype in ("bf16", "fp16"):
+        qkv = torch.from_numpy(raw).to(wl.DTYPES[x_dtype])
+        qg, kg = wl.norm_weights(71, D)
+        cos, sin = tables(np.arange(T) * 13, (D // 2,), D, "interleaved")
+        out = run_fused(qkv, qg, kg, cos, sin, "interleaved")
+        got = _decode(out, x_dtype).reshape(T, 3, H, D)
+        assert np.all(got[0, 0] == 0) and np.all(got[1, 1] == 0)
+        q_ref, k_ref = oracle_fused(qkv, x_dtype, H, D, qg, kg, cos, sin, "interleaved")
+        check_rounding_bound(got[:, 0], q_ref, x_dtype, "extreme Q " + x_dtype)
+        check_rounding_bound(got[:, 1], k_ref, x_dtype, "extreme K " + x_dtype)
+
+
+def test_fp16_subnormal_inputs():
+    T, H, D = 16, 3, 64
+    rng = np.random.default_rng(80)
+    raw = (rng.standard_normal((T, H, D)) * 3e-5).astype(np.float32)   # mostly subnormal fp16
+    q = torch.from_numpy(raw).to(torch.float16)
+    assert ((wl.u16(q) & 0x7C00) == 0).mean() > 0.5
+    qg, _ = wl.norm_weights(81, D)
+    cos, sin = tables(np.arange(T), (D // 2,), D, "interleaved")
+    qd = dev(q)
+    qkr.qknorm_rope_fused(q=qd, q_gamma=dev(qg), cos=dev(cos), sin=dev(sin), eps=1e-10)
+    torch.cuda.synchronize()
+    ref = oracle.qknorm_rope(wl.u16(q), "fp16", row_stride=H * D, col0=0, heads=H, head_dim=D,
+                             gamma=qg.numpy(), eps=1e-10, cos=cos.numpy(), sin=sin.numpy())
+    check_close(_decode(qd, "fp16"), ref, "fp16", "subnormal")
+
+
+def test_side_stream():
+    T, H, D = 300, 8, 128
+    qkv = wl.fused_qkv(90, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(90, D)
+    cos, sin = tables(np.arange(T), (D // 2,), D, "interleaved")
+    st = torch.cuda.Stream()
+    x = dev(qkv)
+    g1, g2, c, s = dev(qg), dev(kg), dev(cos), dev(sin)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        qkr.qknorm_rope_fused(x, q_gamma=g1, k_gamma=g2, cos=c, sin=s, stream=st)
+    st.synchronize()
+    compare_fused(x.cpu(), qkv, "bf16", H, D, qg, kg, cos, sin, "interleaved", what="stream")
+
+
+def test_misaligned_pointer_is_rejected_and_nothing_changes():
+    T, H, D = 8, 2, 64
+    buf = torch.randn(T * 3 * H * D + 8, device=DEV).to(torch.bfloat16)
+    before = buf.clone()
+    x = buf[1:1 + T * 3 * H * D].view(T, 3 * H * D)          # 2-byte offset
+    g = torch.ones(D, device=DEV)
+    c = torch.ones(T, D, device=DEV)
+    with pytest.raises(qkr.QkrError) as e:
+        qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c)
+    assert e.value.status == qkr.binding.QKR_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert torch.equal(buf.view(torch.int16), before.view(torch.int16))
