@@ -13,7 +13,12 @@ oracle on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                   [--layout shared|per_head] [--style interleaved|rotate_half]
-                  [--no-cpu-baseline] [--calib-copy]
+                  [--dtype bf16|fp16] [--flush] [--no-cpu-baseline] [--calib-copy]
+
+Other workloads (tiny, mid, flux, large) are reported the same way; with
+--flush a 1 GiB buffer is rewritten before every timed call (outside that
+call's event bracket) so that inputs smaller than the 256 MB Infinity Cache
+come from HBM, and ``value`` then uses the per-call event times.
 """
 from __future__ import annotations
 
@@ -61,6 +66,10 @@ def parse():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--layout", default="shared", choices=["shared", "per_head"])
     ap.add_argument("--style", default=None, choices=[None, "interleaved", "rotate_half"])
+    ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
+    ap.add_argument("--cos-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--flush", action="store_true",
+                    help="rewrite 1 GiB before each timed call (cache-cold inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget for the CPU-oracle sample")
@@ -84,7 +93,7 @@ def calib_copy(steps: int):
                       "copy_GBps": round(2 * n / dt / 1e9, 1), "steps": steps}))
 
 
-def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s):
+def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
     """Time the fp64 oracle on the same workload: whole passes over every
     token (Q and K), repeated until ``budget_s`` is spent; median pass time."""
     import numpy as np
@@ -102,7 +111,7 @@ def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s):
         for a in range(0, T, chunk):
             b = min(T, a + chunk)
             for col0, g in ((0, qg), (H * D, kg)):
-                oracle.qknorm_rope(bits, "bf16", row_stride=3 * H * D, col0=col0, heads=H,
+                oracle.qknorm_rope(bits, dtype, row_stride=3 * H * D, col0=col0, heads=H,
                                    head_dim=D, gamma=g.numpy(), eps=wl.EPS, cos=c_np, sin=s_np,
                                    style=style, t_begin=a, t_end=b, out=out[:b - a])
         dt = time.perf_counter() - t0
@@ -137,25 +146,38 @@ def main():
     qkr.load_library()
     w = wl.WORKLOADS[args.workload]
     style = args.style or w.styles[0]
+    dtype = args.dtype or w.dtypes[0]
     H, D, T = w.heads, w.head_dim, w.tokens
-    assert w.layout == "fused", "bench times the fused QKV workloads"
     dev = torch.device("cuda:0")
 
-    qkv_cpu = wl.fused_qkv(w.seed, T, H, D, "bf16")
     qg, kg = wl.norm_weights(w.seed, D)
     cos, sin = wl.workload_tables(w, style)
-    x = qkv_cpu.to(dev)
     g1, g2 = qg.to(dev), kg.to(dev)
-    c, s = cos.to(dev), sin.to(dev)
+    cos_bytes = 4
+    if args.cos_dtype == "bf16":
+        cos_t, sin_t = wl.workload_tables(w, style, dtype="bf16")
+        c, s = cos_t.to(dev), sin_t.to(dev)
+        cos_bytes = 2
+    else:
+        c, s = cos.to(dev), sin.to(dev)
     if args.layout == "per_head":
         c, s = wl.expand_per_head(c, H), wl.expand_per_head(s, H)
-    nbytes = wl.algorithmic_bytes(T, H, D, cos_layout=args.layout)
+    qkv_cpu = None
+    if w.layout == "fused":
+        qkv_cpu = wl.fused_qkv(w.seed, T, H, D, dtype)
+        x = qkv_cpu.to(dev)
+        tensors = dict(qkv=x)
+    else:
+        q_cpu, k_cpu = wl.separate_qk(w.seed, T, H, D, (dtype,))[dtype]
+        tensors = dict(q=q_cpu.to(dev), k=k_cpu.to(dev))
+    nbytes = wl.algorithmic_bytes(T, H, D, cos_layout=args.layout, cos_bytes=cos_bytes)
 
     stream = torch.cuda.Stream(device=dev)
     handle = stream.cuda_stream
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
 
     def launch():
-        qkr.qknorm_rope_fused(x, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS,
+        qkr.qknorm_rope_fused(**tensors, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS,
                               style=style, cos_layout=args.layout, stream=handle)
 
     torch.cuda.synchronize()
@@ -172,6 +194,9 @@ def main():
     wall0 = time.perf_counter()
     region0.record(stream)
     for i in range(K):
+        if flush_buf is not None:
+            with torch.cuda.stream(stream):
+                flush_buf.fill_(float(i))
         starts[i].record(stream)
         launch()
         ends[i].record(stream)
@@ -183,8 +208,11 @@ def main():
     per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3   # µs
     mean_us = float(per.mean())
     achieved = nbytes / (mean_us * 1e-6) / 1e9
-    value = nbytes * K / (region_ms * 1e-3) / 1e9
-    info = qkr.kernel_info(D, args.layout, qkr.binding.QKR_FP32, style, qkr.binding.QKR_BF16)
+    # with flushing, the region also holds the flush writes: use the call times
+    value = achieved if args.flush else nbytes * K / (region_ms * 1e-3) / 1e9
+    info = qkr.kernel_info(D, args.layout,
+                           qkr.binding.QKR_BF16 if cos_bytes == 2 else qkr.binding.QKR_FP32, style,
+                           qkr.binding.QKR_FP16 if dtype == "fp16" else qkr.binding.QKR_BF16)
 
     traffic = measured_traffic(args.workload, args.layout, style)
     result = {
@@ -198,10 +226,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "%s: fused QKV bf16 [%d, 3x%dx%d], %s RoPE, %s fp32 cos/sin"
-                               % (w.key, T, H, D, style, args.layout),
+        "config": {"workload": "%s: %s %s [%d, %s%dx%d], %s RoPE, %s %s cos/sin%s"
+                               % (w.key, "fused QKV" if w.layout == "fused" else "separate q, k",
+                                  dtype, T, "3x" if w.layout == "fused" else "", H, D, style,
+                                  args.layout, args.cos_dtype,
+                                  ", cache flushed" if args.flush else ""),
                    "tokens": T, "heads": H, "head_dim": D, "layout": args.layout,
                    "style": style, "math": "f32", "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
@@ -215,9 +246,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic},
     }
-    if not args.no_cpu_baseline:
+    if (not args.no_cpu_baseline and qkv_cpu is not None and args.layout == "shared"
+            and args.cos_dtype == "fp32"):
         result["cpu_baseline"] = cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style,
-                                              args.cpu_seconds)
+                                              args.cpu_seconds, dtype)
     print(json.dumps(result))
     return 0
 

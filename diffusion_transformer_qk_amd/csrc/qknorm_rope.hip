@@ -35,17 +35,16 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlock = kWave * kWavesPerBlock;
 constexpr int kVec = 8;                 // 16-bit elements per 16-byte access
 constexpr int kInterleaved = QKR_ROPE_INTERLEAVED;
 constexpr int kRotateHalf = QKR_ROPE_ROTATE_HALF;
-constexpr int kUnrollShared = 8;        // head iterations in flight per lane (shared)
-constexpr int kUnrollPerHead = 4;       // (per-head layout also loads its cos/sin rows)
+constexpr int kXcds = 8;                // accelerator dies of an MI355X, each with its own L2
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Params {
     uint16_t* x[2];            // tensor s: element (t, h, d) at x[s] + t*row_stride + h*D + d
@@ -93,27 +92,47 @@ __device__ __forceinline__ float half_head_partner(float v)
                                                                      0x101F));  // lane ^ 4
 }
 
-template <bool FP16>
-__device__ __forceinline__ void unpack8(const uint4 v, float f[8])
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void* p)
 {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const u32x4* q = static_cast<const u32x4*>(p);
+    if constexpr (NT)
+        return __builtin_nontemporal_load(q);
+    else
+        return *q;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(void* p, u32x4 v)
+{
+    u32x4* q = static_cast<u32x4*>(p);
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, q);
+    else
+        *q = v;
+}
+
+template <bool FP16>
+__device__ __forceinline__ void unpack8(const u32x4 v, float f[8])
+{
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+        const uint32_t w = v[k];
         if constexpr (FP16) {
-            const f16x2 h = __builtin_bit_cast(f16x2, w[k]);
+            const f16x2 h = __builtin_bit_cast(f16x2, w);
             f[2 * k] = (float)h.x;
             f[2 * k + 1] = (float)h.y;
         } else {
-            f[2 * k] = __uint_as_float(w[k] << 16);
-            f[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+            f[2 * k] = __uint_as_float(w << 16);
+            f[2 * k + 1] = __uint_as_float(w & 0xffff0000u);
         }
     }
 }
 
 template <bool FP16>
-__device__ __forceinline__ uint4 pack8(const float o[8])
+__device__ __forceinline__ u32x4 pack8(const float o[8])
 {
-    uint32_t w[4];
+    u32x4 w;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const f32x2 pr = {o[2 * k], o[2 * k + 1]};
@@ -122,15 +141,37 @@ __device__ __forceinline__ uint4 pack8(const float o[8])
         else
             w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
     }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return w;
 }
 
 __device__ __forceinline__ void load_f32x8(const float* p, float f[8])
 {
-    const float4 a = reinterpret_cast<const float4*>(p)[0];
-    const float4 b = reinterpret_cast<const float4*>(p)[1];
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
+    const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = a[i];
+        f[4 + i] = b[i];
+    }
+}
+
+// 16-byte vectors holding eight table entries: one for bf16, two for fp32.
+template <bool BF16_TABLE>
+constexpr int table_vecs() { return BF16_TABLE ? 1 : 2; }
+
+// Widen eight table entries held in table_vecs() raw vectors starting at w[0].
+template <bool BF16_TABLE>
+__device__ __forceinline__ void widen_table(const u32x4* w, float f[8])
+{
+    if constexpr (BF16_TABLE) {
+        unpack8<false>(w[0], f);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = __uint_as_float(w[0][i]);
+            f[4 + i] = __uint_as_float(w[1][i]);
+        }
+    }
 }
 
 // Eight consecutive table entries starting at element `index`, widened to fp32.
@@ -138,7 +179,7 @@ template <bool BF16_TABLE>
 __device__ __forceinline__ void load_table8(const void* table, int64_t index, float f[8])
 {
     if constexpr (BF16_TABLE)
-        unpack8<false>(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(table) + index), f);
+        unpack8<false>(load16<false>(static_cast<const uint16_t*>(table) + index), f);
     else
         load_f32x8(static_cast<const float*>(table) + index, f);
 }
@@ -160,7 +201,7 @@ __device__ __forceinline__ void rotation_coeffs(const float g[8], const float gp
 
 // One head's slice in this lane: 8 elements in, 8 rotated, normalised out.
 template <int D, int STYLE, bool X_FP16>
-__device__ __forceinline__ uint4 head_math(const uint4 v, const float A[8], const float B[8], float eps)
+__device__ __forceinline__ u32x4 head_math(const u32x4 v, const float A[8], const float B[8], float eps)
 {
     constexpr int L = D / kVec;
     float f[8];
@@ -184,29 +225,129 @@ __device__ __forceinline__ uint4 head_math(const uint4 v, const float A[8], cons
     return pack8<X_FP16>(o);
 }
 
-// ---------------------------------------------------------------- the kernel
-
-template <int D, int STYLE, bool PER_HEAD, bool COS_BF16, bool X_FP16, int U>
-__global__ __launch_bounds__(kBlock) void qknorm_rope_kernel(const Params p)
+// Logical block of hardware block `bid`.  The dispatcher deals consecutive
+// hardware blocks to consecutive dies; ORDER remaps that so each die walks
+// memory in runs:
+//   0   hardware order (die d gets blocks d, d+8, d+16, ...);
+//   -1  one contiguous run of blocks per die;
+//   C>0 runs of C consecutive blocks dealt to the dies in turn (the last,
+//       partial round keeps hardware order).
+template <int ORDER>
+__device__ __forceinline__ int64_t logical_block(uint32_t bid, uint32_t blocks)
 {
-    constexpr int L = D / kVec;       // lanes per head
-    constexpr int HPI = kWave / L;    // heads per wave iteration
-    __shared__ float stage[PER_HEAD ? 4 : kWavesPerBlock * 2 * D];   // [token][cos | sin][D]
+    if constexpr (ORDER == 0) {
+        return bid;
+    } else if constexpr (ORDER < 0) {
+        const uint32_t die = bid % kXcds, local = bid / kXcds;
+        const uint32_t q = blocks / kXcds, r = blocks % kXcds;
+        return (int64_t)die * q + (die < r ? die : r) + local;
+    } else {
+        constexpr uint32_t round = (uint32_t)ORDER * kXcds;
+        if (bid >= blocks / round * round)
+            return bid;
+        const uint32_t die = bid % kXcds, local = bid / kXcds;
+        return ((int64_t)(local / ORDER) * kXcds + die) * ORDER + local % ORDER;
+    }
+}
+
+// Issue the loads of U head iterations starting at head h0 (plus, for the
+// per-head layout, their cos/sin rows); heads past the end read as zero.
+// tw holds, per head iteration u, the cos vectors then the sin vectors.
+template <int D, bool PER_HEAD, bool COS_BF16, int U, int NT, int TW>
+__device__ __forceinline__ void load_chunk(const Params& p, const uint16_t* row, int64_t t, int h0,
+                                           int hs, int d0, u32x4 (&v)[U], u32x4 (&tw)[TW])
+{
+    constexpr int HPI = kWave / (D / kVec);
+    const int H = p.heads;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int h = h0 + u * HPI + hs;
+        if (h < H) {
+            v[u] = load16<(NT & 1) != 0>(row + h * D + d0);
+            if constexpr (PER_HEAD) {
+                constexpr int NV = table_vecs<COS_BF16>();
+                const int64_t idx = (t * H + h) * D + d0;
+                const int per = COS_BF16 ? 8 : 4;          // entries per vector
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    tw[(2 * u) * NV + i] = COS_BF16
+                        ? load16<false>(static_cast<const uint16_t*>(p.cos) + idx + i * per)
+                        : load16<false>(static_cast<const float*>(p.cos) + idx + i * per);
+                    tw[(2 * u + 1) * NV + i] = COS_BF16
+                        ? load16<false>(static_cast<const uint16_t*>(p.sin) + idx + i * per)
+                        : load16<false>(static_cast<const float*>(p.sin) + idx + i * per);
+                }
+            }
+        } else {
+            v[u] = u32x4{0, 0, 0, 0};
+            if constexpr (PER_HEAD) {
+                constexpr int NV = table_vecs<COS_BF16>();
+#pragma unroll
+                for (int i = 0; i < 2 * NV; ++i)
+                    tw[2 * u * NV + i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- the kernel
+//
+// U      head iterations (of 64/L heads per wave) whose loads are in flight
+//        before any arithmetic;
+// WAVES  waves per workgroup (WAVES/2 tokens of Q and K per workgroup);
+// NT     non-temporal Q/K accesses: bit 0 loads, bit 1 stores;
+// ORDER  block order across dies (logical_block).
+
+template <int D, int STYLE, bool PER_HEAD, bool COS_BF16, bool X_FP16, int U, int WAVES, int NT,
+          int ORDER>
+__global__ __launch_bounds__(WAVES * kWave) void qknorm_rope_kernel(const Params p)
+{
+    constexpr int L = D / kVec;        // lanes per head
+    constexpr int HPI = kWave / L;     // heads per wave iteration
+    constexpr int kThreads = WAVES * kWave;
+    constexpr int TU = PER_HEAD ? U : 1;
+    __shared__ float stage[PER_HEAD ? 4 : WAVES * 2 * D];   // [token][cos | sin][D]
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int two = p.n_tensors == 2 ? 1 : 0;
-    const int tokens_per_block = kWavesPerBlock >> two;
-    const int64_t t_first = (int64_t)blockIdx.x * tokens_per_block;
+    const int tokens_per_block = WAVES >> two;
+    const int64_t block = logical_block<ORDER>(blockIdx.x, gridDim.x);
+    const int64_t t_first = block * tokens_per_block;
     const int64_t t = t_first + (wave >> two);
     const int s = wave & two;
+    const bool active = t < p.tokens;
+
+    const int d0 = (lane % L) * kVec;  // this lane's first dimension
+    const int hs = lane / L;           // head slot within a wave iteration
+    const int H = p.heads;
+    uint16_t* const row = p.x[s] + (active ? t : 0) * p.row_stride;
+
+    u32x4 v[U];
+    u32x4 tw[TU * 2 * table_vecs<COS_BF16>()];    // per-head cos/sin rows (raw)
+
+    // Head loads first: they depend on nothing, so their latency overlaps
+    // the staging of the cos/sin rows and the barrier below.
+    float g[8], gp[8];
+    if (active) {
+        load_chunk<D, PER_HEAD, COS_BF16, U, NT>(p, row, t, 0, hs, d0, v, tw);
+        const float* gam = p.gamma[s];
+        load_f32x8(gam + d0, g);
+        if constexpr (STYLE == kInterleaved) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                gp[i] = g[i ^ 1];
+        } else {
+            load_f32x8(gam + (d0 + D / 2) % D, gp);
+        }
+    }
 
     if constexpr (!PER_HEAD) {
         constexpr int per_chunk = COS_BF16 ? 8 : 4;      // table entries per 16-byte chunk
         constexpr int chunks = D / per_chunk;            // chunks per table row
         const int n_chunks = tokens_per_block * 2 * chunks;
-        for (int i = tid; i < n_chunks; i += kBlock) {
+        for (int i = tid; i < n_chunks; i += kThreads) {
             const int r = i / (2 * chunks);
             const int tab = (i / chunks) & 1;
             const int c = i % chunks;
@@ -217,31 +358,18 @@ __global__ __launch_bounds__(kBlock) void qknorm_rope_kernel(const Params p)
                 if constexpr (COS_BF16) {
                     float f[8];
                     load_table8<true>(src, tt * D + c * per_chunk, f);
-                    reinterpret_cast<float4*>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
-                    reinterpret_cast<float4*>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+                    reinterpret_cast<f32x4*>(dst)[0] = f32x4{f[0], f[1], f[2], f[3]};
+                    reinterpret_cast<f32x4*>(dst)[1] = f32x4{f[4], f[5], f[6], f[7]};
                 } else {
-                    *reinterpret_cast<float4*>(dst) =
-                        reinterpret_cast<const float4*>(static_cast<const float*>(src) + tt * D)[c];
+                    *reinterpret_cast<f32x4*>(dst) =
+                        reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + tt * D)[c];
                 }
             }
         }
         __syncthreads();
     }
-    if (t >= p.tokens)
+    if (!active)
         return;
-
-    const int d0 = (lane % L) * kVec;   // this lane's first dimension
-    const int hs = lane / L;            // head slot within a wave iteration
-    const float* gam = p.gamma[s];
-    float g[8], gp[8];
-    load_f32x8(gam + d0, g);
-    if constexpr (STYLE == kInterleaved) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            gp[i] = g[i ^ 1];
-    } else {
-        load_f32x8(gam + (d0 + D / 2) % D, gp);
-    }
 
     float A[8], B[8];
     if constexpr (!PER_HEAD) {
@@ -252,46 +380,38 @@ __global__ __launch_bounds__(kBlock) void qknorm_rope_kernel(const Params p)
         rotation_coeffs<D, STYLE>(g, gp, c, sn, d0, A, B);
     }
 
-    uint16_t* const row = p.x[s] + t * p.row_stride;
-    const int H = p.heads;
-    for (int h0 = 0; h0 < H; h0 += HPI * U) {
-        uint4 v[U];
-        float tc[PER_HEAD ? U : 1][8], ts[PER_HEAD ? U : 1][8];
+    for (int h0 = 0;;) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int h = h0 + u * HPI + hs;
-            if (h < H) {
-                v[u] = *reinterpret_cast<const uint4*>(row + h * D + d0);
-                if constexpr (PER_HEAD) {
-                    const int64_t idx = (t * H + h) * D + d0;
-                    load_table8<COS_BF16>(p.cos, idx, tc[u]);
-                    load_table8<COS_BF16>(p.sin, idx, ts[u]);
-                }
-            } else {
-                v[u] = make_uint4(0, 0, 0, 0);
-                if constexpr (PER_HEAD) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        tc[u][i] = ts[u][i] = 0.0f;
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int h = h0 + u * HPI + hs;
-            uint4 out;
+            u32x4 out;
             if constexpr (PER_HEAD) {
-                float Ah[8], Bh[8];
-                rotation_coeffs<D, STYLE>(g, gp, tc[u], ts[u], d0, Ah, Bh);
+                constexpr int NV = table_vecs<COS_BF16>();
+                float c[8], sn[8], Ah[8], Bh[8];
+                widen_table<COS_BF16>(&tw[2 * u * NV], c);
+                widen_table<COS_BF16>(&tw[(2 * u + 1) * NV], sn);
+                rotation_coeffs<D, STYLE>(g, gp, c, sn, d0, Ah, Bh);
                 out = head_math<D, STYLE, X_FP16>(v[u], Ah, Bh, p.eps);
             } else {
                 out = head_math<D, STYLE, X_FP16>(v[u], A, B, p.eps);
             }
             if (h < H)
-                *reinterpret_cast<uint4*>(row + h * D + d0) = out;
+                store16<(NT & 2) != 0>(row + h * D + d0, out);
         }
+        h0 += HPI * U;
+        if (h0 >= H)
+            break;
+        load_chunk<D, PER_HEAD, COS_BF16, U, NT>(p, row, t, h0, hs, d0, v, tw);
     }
 }
+
+// Launch configuration of the library's kernels.
+constexpr int kUnrollShared = 10;       // head iterations in flight per lane (shared rows)
+constexpr int kUnrollPerHead = 4;       // per-head layout also loads two table rows per head
+constexpr int kWavesPerBlock = 4;
+constexpr int kNonTemporal = 3;         // loads and stores of Q/K bypass cache retention
+constexpr int kBlockOrder = -1;         // one contiguous run of tokens per die
+constexpr int kBlock = kWavesPerBlock * kWave;
 
 // ---------------------------------------------------------------- dispatch
 
@@ -300,7 +420,8 @@ using KernelFn = void (*)(Params);
 template <int D, int STYLE, bool PH, bool CB, bool XF>
 KernelFn kernel_ptr()
 {
-    return qknorm_rope_kernel<D, STYLE, PH, CB, XF, PH ? kUnrollPerHead : kUnrollShared>;
+    return qknorm_rope_kernel<D, STYLE, PH, CB, XF, PH ? kUnrollPerHead : kUnrollShared,
+                              kWavesPerBlock, kNonTemporal, kBlockOrder>;
 }
 
 template <int D, int STYLE, bool PH, bool CB>
@@ -457,7 +578,7 @@ extern "C" int qknorm_rope_kernel_info(int32_t head_dim, int32_t cos_layout, int
     out->lds_bytes = (int32_t)attr.sharedSizeBytes;
     out->scratch_bytes = (int32_t)attr.localSizeBytes;
     out->block_threads = kBlock;
-    out->tokens_per_block = kWavesPerBlock / 2;
+    out->tokens_per_block = kWavesPerBlock / 2;   // fused mode (Q and K per token)
     out->heads_in_flight = cos_layout == QKR_COS_PER_HEAD ? kUnrollPerHead : kUnrollShared;
     return QKR_OK;
 }
