@@ -212,7 +212,8 @@ def main():
     value = achieved if args.flush else nbytes * K / (region_ms * 1e-3) / 1e9
     info = qkr.kernel_info(D, args.layout,
                            qkr.binding.QKR_BF16 if cos_bytes == 2 else qkr.binding.QKR_FP32, style,
-                           qkr.binding.QKR_FP16 if dtype == "fp16" else qkr.binding.QKR_BF16)
+                           qkr.binding.QKR_FP16 if dtype == "fp16" else qkr.binding.QKR_BF16,
+                           heads=H, tokens=T)
 
     traffic = measured_traffic(args.workload, args.layout, style)
     result = {

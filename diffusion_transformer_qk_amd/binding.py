@@ -37,7 +37,8 @@ class QkrError(RuntimeError):
 class KernelInfo(ctypes.Structure):
     _fields_ = [("num_vgprs", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("scratch_bytes", ctypes.c_int32), ("block_threads", ctypes.c_int32),
-                ("tokens_per_block", ctypes.c_int32), ("heads_in_flight", ctypes.c_int32)]
+                ("tokens_per_block", ctypes.c_int32), ("heads_in_flight", ctypes.c_int32),
+                ("die_runs", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,7 +62,8 @@ def load_library(path: str = LIB_PATH):
     lib.qknorm_rope_strerror.restype = ctypes.c_char_p
     lib.qknorm_rope_version.argtypes = []
     lib.qknorm_rope_version.restype = ctypes.c_int
-    lib.qknorm_rope_kernel_info.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(KernelInfo)]
+    lib.qknorm_rope_kernel_info.argtypes = [i32, i32, i64, i32, i32, i32, i32,
+                                            ctypes.POINTER(KernelInfo)]
     lib.qknorm_rope_kernel_info.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -188,9 +190,11 @@ def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
 
 
 def kernel_info(head_dim: int = 128, cos_layout: str = "shared", cos_dtype: int = QKR_FP32,
-                style: str = "interleaved", dtype: int = QKR_BF16) -> dict:
-    """Registers, LDS and scratch of the kernel a configuration launches."""
+                style: str = "interleaved", dtype: int = QKR_BF16, heads: int = 40,
+                tokens: int = 32760) -> dict:
+    """Registers, LDS, scratch and schedule of the kernel a fused-QKV call launches."""
     info = KernelInfo()
-    _check(load_library().qknorm_rope_kernel_info(head_dim, LAYOUTS[cos_layout], cos_dtype,
-                                                  STYLES[style], dtype, ctypes.byref(info)))
+    _check(load_library().qknorm_rope_kernel_info(head_dim, heads, tokens, LAYOUTS[cos_layout],
+                                                  cos_dtype, STYLES[style], dtype,
+                                                  ctypes.byref(info)))
     return {name: getattr(info, name) for name, _ in KernelInfo._fields_}

@@ -226,27 +226,18 @@ __device__ __forceinline__ u32x4 head_math(const u32x4 v, const float A[8], cons
 }
 
 // Logical block of hardware block `bid`.  The dispatcher deals consecutive
-// hardware blocks to consecutive dies; ORDER remaps that so each die walks
-// memory in runs:
-//   0   hardware order (die d gets blocks d, d+8, d+16, ...);
-//   -1  one contiguous run of blocks per die;
-//   C>0 runs of C consecutive blocks dealt to the dies in turn (the last,
-//       partial round keeps hardware order).
+// hardware blocks to consecutive dies; ORDER < 0 remaps that so each die
+// walks one contiguous run of blocks (die d gets the d-th eighth of the grid,
+// the first blocks % 8 dies one block more); ORDER == 0 keeps hardware order.
 template <int ORDER>
 __device__ __forceinline__ int64_t logical_block(uint32_t bid, uint32_t blocks)
 {
     if constexpr (ORDER == 0) {
         return bid;
-    } else if constexpr (ORDER < 0) {
+    } else {
         const uint32_t die = bid % kXcds, local = bid / kXcds;
         const uint32_t q = blocks / kXcds, r = blocks % kXcds;
         return (int64_t)die * q + (die < r ? die : r) + local;
-    } else {
-        constexpr uint32_t round = (uint32_t)ORDER * kXcds;
-        if (bid >= blocks / round * round)
-            return bid;
-        const uint32_t die = bid % kXcds, local = bid / kXcds;
-        return ((int64_t)(local / ORDER) * kXcds + die) * ORDER + local % ORDER;
     }
 }
 
@@ -296,7 +287,7 @@ __device__ __forceinline__ void load_chunk(const Params& p, const uint16_t* row,
 //        before any arithmetic;
 // WAVES  waves per workgroup (WAVES/2 tokens of Q and K per workgroup);
 // NT     non-temporal Q/K accesses: bit 0 loads, bit 1 stores;
-// ORDER  block order across dies (logical_block).
+// ORDER  block order across dies (logical_block): 0 hardware, -1 die runs.
 
 template <int D, int STYLE, bool PER_HEAD, bool COS_BF16, bool X_FP16, int U, int WAVES, int NT,
           int ORDER>
@@ -406,45 +397,101 @@ __global__ __launch_bounds__(WAVES * kWave) void qknorm_rope_kernel(const Params
 }
 
 // Launch configuration of the library's kernels.
-constexpr int kUnrollShared = 10;       // head iterations in flight per lane (shared rows)
-constexpr int kUnrollPerHead = 4;       // per-head layout also loads two table rows per head
 constexpr int kWavesPerBlock = 4;
-constexpr int kNonTemporal = 3;         // loads and stores of Q/K bypass cache retention
-constexpr int kBlockOrder = -1;         // one contiguous run of tokens per die
 constexpr int kBlock = kWavesPerBlock * kWave;
+constexpr int kNonTemporal = 3;         // Q/K loads and stores are not retained in cache
+constexpr int kUnrollPerHead = 4;       // per-head layout also keeps 2 table rows per head
+constexpr int kDieRunsFromBlocks = 4096;
 
 // ---------------------------------------------------------------- dispatch
+//
+// Scheduling only (every choice computes bit-identical output):
+//   unroll  the smallest of {3, 6, 10, 12} head iterations covering all H
+//           heads (capped at 12), so a wave keeps one slice's loads in flight
+//           with few padded iterations; the per-head layout uses 4;
+//   order   one contiguous run of tokens per die when one buffer is streamed
+//           (fused QKV or a single tensor) and the grid has at least
+//           kDieRunsFromBlocks workgroups; hardware order otherwise (two
+//           separate q/k buffers, or small grids where per-die runs are short).
 
 using KernelFn = void (*)(Params);
 
-template <int D, int STYLE, bool PH, bool CB, bool XF>
-KernelFn kernel_ptr()
+struct Launch {
+    int unroll;
+    int order;
+    int64_t blocks;
+    int tokens_per_block;
+};
+
+Launch plan_launch(int head_dim, int heads, int64_t tokens, int n_tensors, bool separate_pair,
+                   bool per_head)
 {
-    return qknorm_rope_kernel<D, STYLE, PH, CB, XF, PH ? kUnrollPerHead : kUnrollShared,
-                              kWavesPerBlock, kNonTemporal, kBlockOrder>;
+    Launch l;
+    const int heads_per_iter = kWave / (head_dim / kVec);
+    const int iters = (heads + heads_per_iter - 1) / heads_per_iter;
+    l.unroll = per_head ? kUnrollPerHead : iters <= 3 ? 3 : iters <= 6 ? 6 : iters <= 10 ? 10 : 12;
+    l.tokens_per_block = kWavesPerBlock / n_tensors;
+    l.blocks = (tokens + l.tokens_per_block - 1) / l.tokens_per_block;
+    l.order = (!separate_pair && l.blocks >= kDieRunsFromBlocks) ? -1 : 0;
+    return l;
+}
+
+template <int D, int STYLE, bool PH, bool CB, bool XF, int ORDER>
+KernelFn kernel_for_unroll(int unroll)
+{
+    if constexpr (PH) {
+        return qknorm_rope_kernel<D, STYLE, PH, CB, XF, kUnrollPerHead, kWavesPerBlock,
+                                  kNonTemporal, ORDER>;
+    } else {
+        if (unroll == 3)
+            return qknorm_rope_kernel<D, STYLE, PH, CB, XF, 3, kWavesPerBlock, kNonTemporal, ORDER>;
+        if (unroll == 6)
+            return qknorm_rope_kernel<D, STYLE, PH, CB, XF, 6, kWavesPerBlock, kNonTemporal, ORDER>;
+        if (unroll == 10)
+            return qknorm_rope_kernel<D, STYLE, PH, CB, XF, 10, kWavesPerBlock, kNonTemporal, ORDER>;
+        return qknorm_rope_kernel<D, STYLE, PH, CB, XF, 12, kWavesPerBlock, kNonTemporal, ORDER>;
+    }
+}
+
+template <int D, int STYLE, bool PH, bool CB, bool XF>
+KernelFn select_order(const Launch& l)
+{
+    return l.order < 0 ? kernel_for_unroll<D, STYLE, PH, CB, XF, -1>(l.unroll)
+                       : kernel_for_unroll<D, STYLE, PH, CB, XF, 0>(l.unroll);
 }
 
 template <int D, int STYLE, bool PH, bool CB>
-KernelFn select_x(bool xf) { return xf ? kernel_ptr<D, STYLE, PH, CB, true>() : kernel_ptr<D, STYLE, PH, CB, false>(); }
-
-template <int D, int STYLE, bool PH>
-KernelFn select_c(bool cb, bool xf) { return cb ? select_x<D, STYLE, PH, true>(xf) : select_x<D, STYLE, PH, false>(xf); }
-
-template <int D, int STYLE>
-KernelFn select_l(bool ph, bool cb, bool xf) { return ph ? select_c<D, STYLE, true>(cb, xf) : select_c<D, STYLE, false>(cb, xf); }
-
-template <int D>
-KernelFn select_s(int style, bool ph, bool cb, bool xf)
+KernelFn select_x(bool xf, const Launch& l)
 {
-    return style == kRotateHalf ? select_l<D, kRotateHalf>(ph, cb, xf) : select_l<D, kInterleaved>(ph, cb, xf);
+    return xf ? select_order<D, STYLE, PH, CB, true>(l) : select_order<D, STYLE, PH, CB, false>(l);
 }
 
-KernelFn select_kernel(int head_dim, int style, int cos_layout, int cos_dtype, int dtype)
+template <int D, int STYLE, bool PH>
+KernelFn select_c(bool cb, bool xf, const Launch& l)
+{
+    return cb ? select_x<D, STYLE, PH, true>(xf, l) : select_x<D, STYLE, PH, false>(xf, l);
+}
+
+template <int D, int STYLE>
+KernelFn select_l(bool ph, bool cb, bool xf, const Launch& l)
+{
+    return ph ? select_c<D, STYLE, true>(cb, xf, l) : select_c<D, STYLE, false>(cb, xf, l);
+}
+
+template <int D>
+KernelFn select_s(int style, bool ph, bool cb, bool xf, const Launch& l)
+{
+    return style == kRotateHalf ? select_l<D, kRotateHalf>(ph, cb, xf, l)
+                                : select_l<D, kInterleaved>(ph, cb, xf, l);
+}
+
+KernelFn select_kernel(int head_dim, int style, int cos_layout, int cos_dtype, int dtype,
+                       const Launch& l)
 {
     const bool ph = cos_layout == QKR_COS_PER_HEAD;
     const bool cb = cos_dtype == QKR_BF16;
     const bool xf = dtype == QKR_FP16;
-    return head_dim == 128 ? select_s<128>(style, ph, cb, xf) : select_s<64>(style, ph, cb, xf);
+    return head_dim == 128 ? select_s<128>(style, ph, cb, xf, l) : select_s<64>(style, ph, cb, xf, l);
 }
 
 int check_config(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype, int32_t style, int32_t dtype)
@@ -534,11 +581,11 @@ extern "C" int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, in
     p.heads = heads;
     p.eps = eps;
 
-    const int tokens_per_block = kWavesPerBlock / p.n_tensors;
-    const int64_t blocks = (tokens + tokens_per_block - 1) / tokens_per_block;
-    KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype);
+    const Launch l = plan_launch(head_dim, heads, tokens, p.n_tensors, !qkv && p.n_tensors == 2,
+                                 cos_layout == QKR_COS_PER_HEAD);
+    KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype, l);
     void* args[] = {&p};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)blocks),
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)l.blocks),
                                      dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
     if (err != hipSuccess)
         return QKR_ERR_HIP;
@@ -562,23 +609,28 @@ extern "C" const char* qknorm_rope_strerror(int status)
 
 extern "C" int qknorm_rope_version(void) { return QKNORM_ROPE_VERSION; }
 
-extern "C" int qknorm_rope_kernel_info(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype,
-                                       int32_t style, int32_t dtype, qkr_kernel_info* out)
+extern "C" int qknorm_rope_kernel_info(int32_t head_dim, int32_t heads, int64_t tokens,
+                                       int32_t cos_layout, int32_t cos_dtype, int32_t style,
+                                       int32_t dtype, qkr_kernel_info* out)
 {
     if (!out)
         return QKR_ERR_NULL;
     const int cfg = check_config(head_dim, cos_layout, cos_dtype, style, dtype);
     if (cfg != QKR_OK)
         return cfg;
+    if (tokens < 0 || tokens >= QKR_MAX_TOKENS || heads < 1 || heads > QKR_MAX_HEADS)
+        return QKR_ERR_SHAPE;
+    const Launch l = plan_launch(head_dim, heads, tokens, 2, false, cos_layout == QKR_COS_PER_HEAD);
     hipFuncAttributes attr;
-    KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype);
+    KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype, l);
     if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn)) != hipSuccess)
         return QKR_ERR_HIP;
     out->num_vgprs = attr.numRegs;
     out->lds_bytes = (int32_t)attr.sharedSizeBytes;
     out->scratch_bytes = (int32_t)attr.localSizeBytes;
     out->block_threads = kBlock;
-    out->tokens_per_block = kWavesPerBlock / 2;   // fused mode (Q and K per token)
-    out->heads_in_flight = cos_layout == QKR_COS_PER_HEAD ? kUnrollPerHead : kUnrollShared;
+    out->tokens_per_block = l.tokens_per_block;
+    out->heads_in_flight = l.unroll;
+    out->die_runs = l.order < 0 ? 1 : 0;
     return QKR_OK;
 }

@@ -103,18 +103,22 @@ typedef struct {
     int32_t lds_bytes;        /* static LDS per workgroup                         */
     int32_t scratch_bytes;    /* private (spill) memory per lane; 0 expected       */
     int32_t block_threads;    /* workgroup size the library launches              */
-    int32_t tokens_per_block; /* tokens one workgroup covers (fused mode)         */
-    int32_t heads_in_flight;  /* head loads each lane keeps in flight              */
+    int32_t tokens_per_block; /* tokens one workgroup covers                      */
+    int32_t heads_in_flight;  /* head iterations whose loads a lane keeps in flight */
+    int32_t die_runs;         /* 1: each die processes one contiguous token run   */
 } qkr_kernel_info;
 
 /*
  * qknorm_rope_kernel_info -- fill *out for the kernel that qknorm_rope_fused
- * would launch for (head_dim, cos_layout, cos_dtype, style, dtype).  Needs a
- * HIP device (queries the loaded code object).  Returns QKR_OK, QKR_ERR_NULL,
- * QKR_ERR_ARG / QKR_ERR_UNSUPPORTED for a bad configuration, or QKR_ERR_HIP.
+ * launches on a fused QKV buffer of `tokens` x 3*`heads`*`head_dim` with the
+ * given layout and dtypes (the unroll depth and block order depend on heads
+ * and tokens).  Needs a HIP device (queries the loaded code object).
+ * Returns QKR_OK, QKR_ERR_NULL, QKR_ERR_ARG / QKR_ERR_UNSUPPORTED /
+ * QKR_ERR_SHAPE for a bad configuration, or QKR_ERR_HIP.
  */
-int qknorm_rope_kernel_info(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype,
-                            int32_t style, int32_t dtype, qkr_kernel_info* out);
+int qknorm_rope_kernel_info(int32_t head_dim, int32_t heads, int64_t tokens, int32_t cos_layout,
+                            int32_t cos_dtype, int32_t style, int32_t dtype,
+                            qkr_kernel_info* out);
 
 #ifdef __cplusplus
 }

@@ -148,12 +148,21 @@ def compare_fused(out, qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout="
 @pytest.mark.parametrize("head_dim", [64, 128])
 @pytest.mark.parametrize("layout", ["shared", "per_head"])
 def test_kernels_do_not_spill(head_dim, layout):
+    """Every instantiation (all unroll depths and block orders) has no scratch."""
+    seen = set()
     for style in ("interleaved", "rotate_half"):
         for cd in (qkr.binding.QKR_FP32, qkr.binding.QKR_BF16):
             for xd in (qkr.binding.QKR_BF16, qkr.binding.QKR_FP16):
-                info = qkr.kernel_info(head_dim, layout, cd, style, xd)
-                assert info["scratch_bytes"] == 0, info
-                assert 0 < info["num_vgprs"] <= 128, info
+                for heads in (1, 24, 40, 48, 72, 100):
+                    for tokens in (64, 100000):
+                        info = qkr.kernel_info(head_dim, layout, cd, style, xd, heads=heads,
+                                               tokens=tokens)
+                        assert info["scratch_bytes"] == 0, info
+                        assert 0 < info["num_vgprs"] <= 128, info
+                        seen.add((info["heads_in_flight"], info["die_runs"]))
+    want = ({(4, 0), (4, 1)} if layout == "per_head" else
+            {(u, o) for u in (3, 6, 10, 12) for o in (0, 1)})
+    assert want <= seen, seen
 
 
 # ----------------------------------------------------------------------------- the five workloads
@@ -262,6 +271,24 @@ def test_large_workload_sampled_and_layout_parity(style):
     assert_v_untouched(out, qkv, H, D)
     m = _check_sampled(out, qkv, H, D, qg, kg, cos, sin, style, 7, "large " + style)
     print("large", style, "sampled max_abs", m)
+
+
+@pytest.mark.parametrize("heads,head_dim", [(3, 128), (24, 128), (48, 128), (72, 64), (100, 64)])
+def test_die_order_every_unroll(heads, head_dim):
+    """8200 tokens = 4100 workgroups: the per-die token runs (with a ragged
+    4100 % 8 remainder) for head counts that select each unroll depth."""
+    T = 8200
+    qkv = wl.fused_qkv(3000 + heads, T, heads, head_dim, "bf16")
+    qg, kg = wl.norm_weights(3000 + heads, head_dim)
+    cos, sin = tables(np.arange(T), (head_dim // 2,), head_dim, "rotate_half")
+    info = qkr.kernel_info(head_dim, "shared", qkr.binding.QKR_FP32, "rotate_half",
+                           qkr.binding.QKR_BF16, heads=heads, tokens=T)
+    assert info["die_runs"] == 1
+    out = run_fused(qkv, qg, kg, cos, sin, "rotate_half")
+    assert_v_untouched(out, qkv, heads, head_dim)
+    m = _check_sampled(out, qkv, heads, head_dim, qg, kg, cos, sin, "rotate_half", heads,
+                       "die order U%d" % info["heads_in_flight"])
+    print("die order heads", heads, "U", info["heads_in_flight"], "max_abs", m)
 
 
 # ----------------------------------------------------------------------------- exact layout parity
@@ -432,3 +459,58 @@ def test_misaligned_pointer_is_rejected_and_nothing_changes():
     assert e.value.status == qkr.binding.QKR_ERR_ALIGN
     torch.cuda.synchronize()
     assert torch.equal(buf.view(torch.int16), before.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- capture and streams
+
+
+def test_graph_capture_replays_match_eager():
+    """The call holds no allocation, copy or synchronisation, so it captures into a
+    HIP graph; every replay must equal the same number of eager calls, bit for bit."""
+    T, H, D = 97, 6, 128
+    qkv = wl.fused_qkv(100, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(100, D)
+    cos, sin = tables(np.arange(T), (D // 2,), D, "interleaved")
+    g1, g2, c, s = dev(qg), dev(kg), dev(cos), dev(sin)
+    x_graph = dev(qkv)
+    x_eager = dev(qkv)
+    st = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=st):
+        qkr.qknorm_rope_fused(x_graph, q_gamma=g1, k_gamma=g2, cos=c, sin=s)
+    torch.cuda.synchronize()
+    # capture does not execute: the buffer is still the input
+    assert torch.equal(x_graph.view(torch.int16), x_eager.view(torch.int16))
+    for replay in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        qkr.qknorm_rope_fused(x_eager, q_gamma=g1, k_gamma=g2, cos=c, sin=s)
+        torch.cuda.synchronize()
+        assert torch.equal(x_graph.view(torch.int16), x_eager.view(torch.int16)), replay
+    # the first application matches the oracle (later ones re-normalise rotated data)
+    once = dev(qkv)
+    qkr.qknorm_rope_fused(once, q_gamma=g1, k_gamma=g2, cos=c, sin=s)
+    torch.cuda.synchronize()
+    compare_fused(once.cpu(), qkv, "bf16", H, D, qg, kg, cos, sin, "interleaved", what="graph")
+
+
+def test_concurrent_streams_are_independent():
+    """Calls on different streams over different buffers do not interfere."""
+    T, H, D = 211, 8, 64
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    cases = []
+    for i, st in enumerate(streams):
+        style = ("interleaved", "rotate_half")[i % 2]
+        qkv = wl.fused_qkv(110 + i, T, H, D, "fp16")
+        qg, kg = wl.norm_weights(110 + i, D)
+        cos, sin = tables(np.arange(T) + 7 * i, (D // 2,), D, style)
+        cases.append((qkv, qg, kg, cos, sin, style, dev(qkv), dev(qg), dev(kg), dev(cos), dev(sin)))
+    torch.cuda.synchronize()
+    for st, (_, _, _, _, _, style, x, g1, g2, c, s) in zip(streams, cases):
+        with torch.cuda.stream(st):
+            qkr.qknorm_rope_fused(x, q_gamma=g1, k_gamma=g2, cos=c, sin=s, style=style,
+                                  stream=st)
+    torch.cuda.synchronize()
+    for qkv, qg, kg, cos, sin, style, x, *_ in cases:
+        compare_fused(x.cpu(), qkv, "fp16", H, D, qg, kg, cos, sin, style, what="streams")
