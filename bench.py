@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--flush", action="store_true",
                     help="rewrite 1 GiB before each timed call (cache-cold inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU-oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
@@ -106,7 +106,7 @@ def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
     out = np.empty((chunk, H, D), dtype=np.float64)
     c_np, s_np = cos.numpy(), sin.numpy()
     passes, spent = [], 0.0
-    while not passes or (spent < budget_s and len(passes) < 50):
+    while not passes or (spent < budget_s and len(passes) < 100):
         t0 = time.perf_counter()
         for a in range(0, T, chunk):
             b = min(T, a + chunk)
