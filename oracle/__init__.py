@@ -1,10 +1,11 @@
-"""CPU oracle for the fused QK-norm + RoPE pass: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the fused QK-norm + RoPE pass and the adaptive layer norm
+with scale/shift: TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its binding) never touches it, and the two share no code.
 
-The arithmetic lives in ``qkr_oracle.c`` (plain C, fp64, OpenMP over tokens);
+The arithmetic lives in ``qkr_oracle.c`` (plain C, fp64, OpenMP over rows);
 this module compiles it with gcc and marshals numpy arrays.
 """
 from __future__ import annotations
@@ -73,6 +74,9 @@ class Oracle:
         lib.qkr_oracle_decode.restype = None
         lib.qkr_oracle_round.argtypes = [p, i64, c_int]
         lib.qkr_oracle_round.restype = None
+        lib.qkr_oracle_adaln.argtypes = [p, c_int, i64, i64, i64, i64, p, p, c_int,
+                                         ctypes.c_float, p]
+        lib.qkr_oracle_adaln.restype = c_int
         lib.qkr_oracle_max_threads.argtypes = []
         lib.qkr_oracle_max_threads.restype = c_int
         self.lib = lib
@@ -132,6 +136,37 @@ class Oracle:
             raise ValueError("oracle rejected its arguments")
         return out
 
+    def adaln(self, x_bits: np.ndarray, x_dtype: str, *, hidden: int, rows_per_batch: int,
+              scale, shift, mod_dtype: str, eps: float, row_begin: int = 0,
+              row_end: int | None = None, out: np.ndarray | None = None) -> np.ndarray:
+        """fp64 [row_end - row_begin, hidden] adaptive layer norm with scale/shift.
+
+        ``scale``/``shift``: [batches, hidden] as float32 (mod_dtype "fp32") or
+        their 16-bit patterns (uint16, "bf16"/"fp16"); row r uses batch
+        r // rows_per_batch.
+        """
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1)
+        rows = x.size // hidden
+        if row_end is None:
+            row_end = rows
+        assert 0 <= row_begin <= row_end <= rows and x.size == rows * hidden
+        want = np.float32 if mod_dtype == "fp32" else np.uint16
+        sc = np.ascontiguousarray(scale)
+        sh = np.ascontiguousarray(shift)
+        assert sc.dtype == want and sh.dtype == want and sc.size == sh.size
+        batches_needed = (row_end - 1) // rows_per_batch + 1 if row_end > row_begin else 0
+        assert sc.size >= batches_needed * hidden, "scale/shift too small"
+        shape = (row_end - row_begin, hidden)
+        if out is None:
+            out = np.empty(shape, dtype=np.float64)
+        assert out.shape == shape and out.dtype == np.float64 and out.flags.c_contiguous
+        rc = self.lib.qkr_oracle_adaln(_ptr(x), DTYPE_CODE[x_dtype], row_begin, row_end, hidden,
+                                       rows_per_batch, _ptr(sc), _ptr(sh), DTYPE_CODE[mod_dtype],
+                                       ctypes.c_float(eps), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return out
+
     def fused_qk(self, qkv_bits: np.ndarray, x_dtype: str, *, heads: int, head_dim: int,
                  q_gamma, k_gamma, eps: float, cos, sin, cos_dtype="fp32",
                  cos_layout="shared", style="interleaved", t_begin=0, t_end=None):
@@ -175,3 +210,7 @@ def qknorm_rope(x_bits, x_dtype, **kw):
 
 def fused_qk(qkv_bits, x_dtype, **kw):
     return default().fused_qk(qkv_bits, x_dtype, **kw)
+
+
+def adaln(x_bits, x_dtype, **kw):
+    return default().adaln(x_bits, x_dtype, **kw)

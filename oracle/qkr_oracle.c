@@ -31,6 +31,9 @@
  * gamma multiplied directly and before RoPE, the +angle sign, no intermediate
  * rounding) are the plain RMSNorm / RoPE definitions.
  *
+ * The file also holds the oracle of the adaptive layer norm with scale and
+ * shift (qkr_oracle_adaln, below).
+ *
  * Every function here is pinned by CPU tests against brute force in exact
  * arithmetic, closed forms, invariants and library routines.
  */
@@ -195,6 +198,67 @@ int qkr_oracle_qknorm_rope(const uint16_t* x, int x_dtype, int64_t row_stride, i
                 oh[a] = nrm[a] * ca - nrm[b] * sa;
                 oh[b] = nrm[b] * cb + nrm[a] * sb;
             }
+        }
+    }
+    return 0;
+}
+
+/* One element of a modulation table: bf16 (0), fp16 (1) or fp32 (2). */
+static double mod_value(const void* table, int dtype, int64_t index)
+{
+    if (dtype == QKR_O_FP32)
+        return (double)((const float*)table)[index];
+    return decode16(((const uint16_t*)table)[index], dtype);
+}
+
+/*
+ * Adaptive layer norm with a per-sample scale and shift: the "fuse_scale_shift"
+ * (AdaLN) step that TensorRT-Model-Connect PR "perf(diffusion): fused qknorm
+ * rope Flux 2.0" lists as its largest follow-up.  The page gives only the
+ * name; this is the plain definition of an AdaLN modulation (layer norm
+ * without learned affine, then (1 + scale) and shift):
+ *
+ *   for row r of x [rows, hidden] (C = hidden), batch b = r / rows_per_batch:
+ *     mean = (sum_c x[c]) / C
+ *     var  = (sum_c (x[c] - mean)^2) / C          biased variance
+ *     n[c] = (x[c] - mean) / sqrt(var + eps)
+ *     y[c] = n[c] * (1 + scale[b, c]) + shift[b, c]
+ *
+ * x: 16-bit (x_dtype 0 bf16, 1 fp16); scale, shift: [batches, C] of
+ * mod_dtype (0 bf16, 1 fp16, 2 fp32).  out: fp64 [row_end - row_begin, C].
+ */
+int qkr_oracle_adaln(const uint16_t* x, int x_dtype, int64_t row_begin, int64_t row_end,
+                     int64_t hidden, int64_t rows_per_batch, const void* scale, const void* shift,
+                     int mod_dtype, float eps, double* out)
+{
+    if (hidden <= 0 || rows_per_batch <= 0 || row_end < row_begin || row_begin < 0)
+        return -1;
+    if (mod_dtype != QKR_O_BF16 && mod_dtype != QKR_O_FP16 && mod_dtype != QKR_O_FP32)
+        return -1;
+    const int64_t C = hidden;
+    const double eps64 = (double)eps;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t r = row_begin; r < row_end; ++r) {
+        const uint16_t* xr = x + r * C;
+        double* yr = out + (r - row_begin) * C;
+        const int64_t b = r / rows_per_batch;
+
+        double sum = 0.0;
+        for (int64_t c = 0; c < C; ++c)
+            sum += decode16(xr[c], x_dtype);
+        const double mean = sum / (double)C;
+        double sum_dev = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const double dev = decode16(xr[c], x_dtype) - mean;
+            sum_dev += dev * dev;
+        }
+        const double var = sum_dev / (double)C;
+        const double inv = 1.0 / sqrt(var + eps64);
+        for (int64_t c = 0; c < C; ++c) {
+            const double n = (decode16(xr[c], x_dtype) - mean) * inv;
+            yr[c] = n * (1.0 + mod_value(scale, mod_dtype, b * C + c))
+                    + mod_value(shift, mod_dtype, b * C + c);
         }
     }
     return 0;

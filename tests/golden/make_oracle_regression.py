@@ -17,6 +17,7 @@ sys.path.insert(0, ROOT)
 import oracle  # noqa: E402
 import workloads as wl  # noqa: E402
 
+ADALN_CASES = [("bf16", "fp32"), ("fp16", "bf16")]
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_regression.txt")
 CASES = [  # (style, x dtype, cos dtype, cos layout, head_dim)
     ("interleaved", "bf16", "fp32", "shared", 64),
@@ -38,6 +39,12 @@ def cases():
                                k_gamma=kg.numpy(), eps=wl.EPS, cos=to_np(c), sin=to_np(s),
                                cos_dtype=cdt, cos_layout=lay, style=style)
         yield "%s %s %s %s %d" % (style, xdt, cdt, lay, d), np.concatenate([q.ravel(), k.ravel()])
+    for xdt, mdt in ADALN_CASES:
+        x, sc, sh = wl.adaln_inputs(4343, 6, 200, 2, xdt, mdt)
+        to_np = (lambda t: t.numpy()) if mdt == "fp32" else wl.u16
+        y = oracle.adaln(wl.u16(x), xdt, hidden=200, rows_per_batch=3, scale=to_np(sc),
+                         shift=to_np(sh), mod_dtype=mdt, eps=wl.EPS)
+        yield "adaln %s %s" % (xdt, mdt), y.ravel()
 
 
 def main():

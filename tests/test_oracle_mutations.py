@@ -79,3 +79,62 @@ def test_mutation_is_caught(tmp_path, name):
     lib = oracle.compile_source(path, os.path.join(tmp_path, "libmut.so"))
     caught = _caught(oracle.Oracle(lib))
     assert caught, "no pin catches mutation " + name
+
+
+# ----------------------------------------------------------------------------- adaptive layer norm
+
+import tests.test_oracle_adaln_pins as adaln_pins  # noqa: E402
+
+ADALN_MUTATIONS = {
+    "adaln_unbiased_variance": ("const double var = sum_dev / (double)C;",
+                                "const double var = sum_dev / (double)(C - 1);"),
+    "adaln_eps_outside_root": ("1.0 / sqrt(var + eps64)", "1.0 / sqrt(var) + eps64"),
+    "adaln_scale_without_one": ("(1.0 + mod_value(scale", "(mod_value(scale"),
+    "adaln_batch_modulo": ("const int64_t b = r / rows_per_batch;",
+                           "const int64_t b = r % rows_per_batch;"),
+    "adaln_shift_read_from_scale": ("+ mod_value(shift, mod_dtype, b * C + c);",
+                                    "+ mod_value(scale, mod_dtype, b * C + c);"),
+    "adaln_mean_not_subtracted": ("const double n = (decode16(xr[c], x_dtype) - mean) * inv;",
+                                  "const double n = decode16(xr[c], x_dtype) * inv;"),
+    "adaln_fp16_mod_decoded_as_bf16": ("return decode16(((const uint16_t*)table)[index], dtype);",
+                                       "return decode16(((const uint16_t*)table)[index], QKR_O_BF16);"),
+    "adaln_drop_last_in_mean": ("for (int64_t c = 0; c < C; ++c)\n            sum += ",
+                                "for (int64_t c = 0; c + 1 < C; ++c)\n            sum += "),
+}
+
+ADALN_PIN_TESTS = [
+    (adaln_pins.test_zero_modulation_is_torch_layer_norm, {"x_dtype": "bf16", "hidden": 64}),
+    (adaln_pins.test_scale_minus_one_gives_shift_exactly, {}),
+    (adaln_pins.test_constant_row_gives_shift_exactly, {}),
+    (adaln_pins.test_output_moments, {}),
+    (adaln_pins.test_affine_invariance, {}),
+    (adaln_pins.test_brute_force, {"x_dtype": "bf16", "mod_dtype": "fp16", "hidden": 24}),
+]
+
+
+def _caught_adaln(variant) -> list:
+    caught = []
+    for fn, kw in ADALN_PIN_TESTS:
+        try:
+            with np.errstate(all="ignore"):
+                fn(variant, **kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+    return caught
+
+
+def test_unmutated_source_passes_every_adaln_pin():
+    assert _caught_adaln(oracle.default()) == []
+
+
+@pytest.mark.parametrize("name", sorted(ADALN_MUTATIONS))
+def test_adaln_mutation_is_caught(tmp_path, name):
+    old, new = ADALN_MUTATIONS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    path = os.path.join(tmp_path, "mut.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new, 1))
+    lib = oracle.compile_source(path, os.path.join(tmp_path, "libmut.so"))
+    assert _caught_adaln(oracle.Oracle(lib)), "no pin catches mutation " + name

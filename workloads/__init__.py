@@ -212,3 +212,79 @@ def algorithmic_bytes(tokens: int, heads: int, head_dim: int, n_tensors: int = 2
     qk = tokens * n_tensors * heads * head_dim * x_bytes * 2
     rows = tokens * (heads if cos_layout == "per_head" else 1)
     return qk + rows * head_dim * cos_bytes * 2
+
+
+# ----------------------------------------------------------------------------- AdaLN modulation
+#
+# Inputs for the fused layer norm + scale/shift (AdaLN) pass:
+#   x[r, c]  = (N(0,1) + bias_c) * s_r, bias_c ~ N(0, 0.5) per channel, s_r the
+#              per-token log-uniform[0.1, 10] scale, fp32 then one RNE cast;
+#   scale, shift [batches, hidden] = 0.5 N(0,1) each, cast to their dtype.
+# Seeds: SeedSequence(seed) spawned into token scale, activations (per block
+# of rows), channel bias, scale, shift.
+
+
+@dataclass(frozen=True)
+class AdalnWorkload:
+    key: str
+    seed: int
+    rows: int
+    hidden: int
+    batches: int
+    dtypes: tuple
+    note: str = field(default="", compare=False)
+
+    @property
+    def rows_per_batch(self) -> int:
+        return self.rows // self.batches
+
+
+ADALN_WORKLOADS = {
+    "adaln_flux": AdalnWorkload("adaln_flux", 1101, 4608, 6144, 1, ("bf16", "fp16"),
+                                note="FLUX.2-dev 1024x1024: 512 text + 4096 image tokens, hidden 48x128"),
+    "adaln_wan": AdalnWorkload("adaln_wan", 1102, 32760, 5120, 1, ("bf16",),
+                               note="Wan A14B 21x30x52 latent tokens, hidden 40x128"),
+    "adaln_wan_cfg2": AdalnWorkload("adaln_wan_cfg2", 1103, 65520, 5120, 2, ("bf16",),
+                                    note="two guidance branches of the Wan shape, one modulation row each"),
+}
+
+
+def _adaln_children(seed: int):
+    return np.random.SeedSequence(seed).spawn(5)   # scale_t, activations, bias, scale, shift
+
+
+def adaln_inputs(seed: int, rows: int, hidden: int, batches: int, dtype: str = "bf16",
+                 mod_dtype: str = "fp32"):
+    """(x [rows, hidden], scale [batches, hidden], shift [batches, hidden]) CPU tensors."""
+    kids = _adaln_children(seed)
+    g = np.random.Generator(np.random.PCG64(kids[0]))
+    s = np.exp(g.uniform(math.log(0.1), math.log(10.0), size=rows)).astype(np.float32)
+    gb = np.random.Generator(np.random.PCG64(kids[2]))
+    bias = (0.5 * gb.standard_normal(hidden)).astype(np.float32)
+    out = np.empty((rows, hidden), dtype=np.float32)
+    n_blocks = -(-rows // ROWS_PER_BLOCK) if rows else 0
+    blocks = kids[1].spawn(n_blocks) if n_blocks else []
+
+    def work(b):
+        lo = b * ROWS_PER_BLOCK
+        hi = min(rows, lo + ROWS_PER_BLOCK)
+        gg = np.random.Generator(np.random.PCG64(blocks[b]))
+        gg.standard_normal((hi - lo, hidden), dtype=np.float32, out=out[lo:hi])
+        out[lo:hi] += bias[None, :]
+        out[lo:hi] *= s[lo:hi, None]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(n_blocks)))
+    x = _cast(out, dtype)
+    mods = []
+    for child in kids[3:5]:
+        gm = np.random.Generator(np.random.PCG64(child))
+        m = (0.5 * gm.standard_normal((batches, hidden))).astype(np.float32)
+        t = torch.from_numpy(m)
+        mods.append(t if mod_dtype == "fp32" else t.to(DTYPES[mod_dtype]))
+    return x, mods[0], mods[1]
+
+
+def adaln_bytes(rows: int, hidden: int, batches: int, x_bytes: int = 2, mod_bytes: int = 4) -> int:
+    """Bytes the pass must move: x read, y written, scale and shift read once."""
+    return rows * hidden * x_bytes * 2 + batches * hidden * mod_bytes * 2
