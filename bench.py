@@ -11,6 +11,8 @@ the K timed steps (GB/s, bytes the pass must move / time);
 around each launch on the launch stream; ``cpu_baseline`` times the fp64 CPU
 oracle on a bounded sample of the same workload.
 
+  python bench.py --op fuse_scale_shift [--workload adaln_wan|adaln_flux|adaln_wan_cfg2]
+                  [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                   [--layout shared|per_head] [--style interleaved|rotate_half]
                   [--dtype bf16|fp16] [--flush] [--no-cpu-baseline] [--calib-copy]
@@ -63,7 +65,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--op", default="qknorm_rope", choices=["qknorm_rope", "fuse_scale_shift"])
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--mod-dtype", default="fp32", choices=["fp32", "bf16", "fp16"])
+    ap.add_argument("--inplace", action="store_true", help="AdaLN: write y over x")
     ap.add_argument("--layout", default="shared", choices=["shared", "per_head"])
     ap.add_argument("--style", default=None, choices=[None, "interleaved", "rotate_half"])
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
@@ -127,6 +132,90 @@ def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
                       % (len(passes), T, 2 * H, chunk)}
 
 
+def time_launches(launch, stream, steps, warmup, flush_buf=None):
+    """Warm up, then time `steps` launches with HIP events on `stream`.
+
+    Returns (per-launch µs array, region ms, wall s)."""
+    import numpy as np
+    import torch
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(steps):
+        if flush_buf is not None:
+            with torch.cuda.stream(stream):
+                flush_buf.fill_(float(i))
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3
+    return per, region0.elapsed_time(region1), wall
+
+
+def bench_fuse_scale_shift(args):
+    """AdaLN modulation on one of the ADALN_WORKLOADS; prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_qk_amd as qkr
+    import workloads as wl
+    w = wl.ADALN_WORKLOADS[args.workload or "adaln_wan"]
+    dtype = args.dtype or w.dtypes[0]
+    dev = torch.device("cuda:0")
+    x_cpu, sc, sh = wl.adaln_inputs(w.seed, w.rows, w.hidden, w.batches, dtype, args.mod_dtype)
+    x = x_cpu.to(dev)
+    scd, shd = sc.to(dev), sh.to(dev)
+    y = x if args.inplace else torch.empty_like(x)
+    mod_bytes = 4 if args.mod_dtype == "fp32" else 2
+    nbytes = wl.adaln_bytes(w.rows, w.hidden, w.batches, mod_bytes=mod_bytes)
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+
+    def launch():
+        qkr.fuse_scale_shift(x, scd, shd, out=y, eps=wl.EPS, rows_per_batch=w.rows_per_batch,
+                             stream=handle)
+
+    per, region_ms, wall = time_launches(launch, stream, args.steps, args.warmup, flush_buf)
+    K = args.steps
+    mean_us = float(per.mean())
+    achieved = nbytes / (mean_us * 1e-6) / 1e9
+    value = achieved if args.flush else nbytes * K / (region_ms * 1e-3) / 1e9
+    result = {
+        "metric": "AdaLN fuse_scale_shift µs/call and achieved HBM GB/s (% of peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(region_ms / K, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s: x %s [%d, %d], %d modulation row(s) %s%s%s"
+                               % (w.key, dtype, w.rows, w.hidden, w.batches, args.mod_dtype,
+                                  ", in place" if args.inplace else "",
+                                  ", cache flushed" if args.flush else ""),
+                   "rows": w.rows, "hidden": w.hidden, "batches": w.batches, "math": "f32",
+                   "parallelism": "single GPU"},
+        "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
+                        "p10": round(float(np.percentile(per, 10)), 2),
+                        "p90": round(float(np.percentile(per, 90)), 2)},
+        "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
+        "bytes_per_call": nbytes, "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(result))
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -144,6 +233,9 @@ def main():
         return 0
 
     qkr.load_library()
+    if args.op == "fuse_scale_shift":
+        return bench_fuse_scale_shift(args)
+    args.workload = args.workload or "headline"
     w = wl.WORKLOADS[args.workload]
     style = args.style or w.styles[0]
     dtype = args.dtype or w.dtypes[0]

@@ -1,13 +1,15 @@
-"""Fused diffusion-transformer QK-norm + RoPE for AMD Instinct MI355X (gfx950).
+"""Fused diffusion-transformer QK-norm + RoPE (and the AdaLN modulation step)
+for AMD Instinct MI355X (gfx950).
 
-The pass runs in hand-written HIP kernels behind the C ABI of
-``include/qknorm_rope.h`` (``libqknorm_rope.so``); this package is the thin
-Python binding over it.
+The passes run in hand-written HIP kernels behind the C ABI of
+``include/qknorm_rope.h`` and ``include/fuse_scale_shift.h``
+(``libqknorm_rope.so``); this package is the thin Python binding over it.
 """
 from .binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, QkrError, kernel_info, load_library, qknorm_rope_fused,
-    qknorm_rope_fused_raw, strerror, version,
+    EXPORTS, LIB_PATH, QkrError, dit_fuse_scale_shift_raw, fuse_scale_shift, kernel_info,
+    load_library, qknorm_rope_fused, qknorm_rope_fused_raw, strerror, version,
 )
 
-__all__ = ["qknorm_rope_fused", "qknorm_rope_fused_raw", "kernel_info", "load_library",
-           "strerror", "version", "QkrError", "EXPORTS", "LIB_PATH"]
+__all__ = ["qknorm_rope_fused", "qknorm_rope_fused_raw", "fuse_scale_shift",
+           "dit_fuse_scale_shift_raw", "kernel_info", "load_library", "strerror", "version",
+           "QkrError", "EXPORTS", "LIB_PATH"]

@@ -1,9 +1,11 @@
 """ctypes binding of ``libqknorm_rope.so`` (argument marshalling only).
 
-Every step of the pass runs in the HIP kernels behind the C ABI declared in
-``include/qknorm_rope.h``; this module turns torch tensors into device
-pointers, sizes and enum codes and raises on a non-zero status.  There is no
-fallback: if the library is missing, loading fails loudly.
+Every step runs in the HIP kernels behind the C ABI declared in
+``include/qknorm_rope.h`` (fused QK-norm + RoPE) and
+``include/fuse_scale_shift.h`` (AdaLN modulation); this module turns torch
+tensors into device pointers, sizes and enum codes and raises on a non-zero
+status.  There is no fallback: if the library is missing, loading fails
+loudly.
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ QKR_ROPE_INTERLEAVED, QKR_ROPE_ROTATE_HALF = 0, 1
 LAYOUTS = {"shared": QKR_COS_SHARED, "per_head": QKR_COS_PER_HEAD}
 STYLES = {"interleaved": QKR_ROPE_INTERLEAVED, "rotate_half": QKR_ROPE_ROTATE_HALF}
 EXPORTS = ("qknorm_rope_fused", "qknorm_rope_strerror", "qknorm_rope_version",
-           "qknorm_rope_kernel_info")
+           "qknorm_rope_kernel_info", "dit_fuse_scale_shift")
+MOD_DTYPES = {"bf16": QKR_BF16, "fp16": QKR_FP16, "fp32": QKR_FP32}
 
 
 class QkrError(RuntimeError):
@@ -65,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.qknorm_rope_kernel_info.argtypes = [i32, i32, i64, i32, i32, i32, i32,
                                             ctypes.POINTER(KernelInfo)]
     lib.qknorm_rope_kernel_info.restype = ctypes.c_int
+    lib.dit_fuse_scale_shift.argtypes = [vp, vp, i64, i32, i64, vp, vp, i32, f32, i32, vp]
+    lib.dit_fuse_scale_shift.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -198,3 +203,61 @@ def kernel_info(head_dim: int = 128, cos_layout: str = "shared", cos_dtype: int 
                                                   cos_dtype, STYLES[style], dtype,
                                                   ctypes.byref(info)))
     return {name: getattr(info, name) for name, _ in KernelInfo._fields_}
+
+
+def dit_fuse_scale_shift_raw(x: int, y: int, rows: int, hidden: int, rows_per_batch: int,
+                             scale: int, shift: int, mod_dtype: int, eps: float, dtype: int,
+                             stream: int) -> int:
+    """The AdaLN C entry point with integer pointers; returns the raw status."""
+    lib = load_library()
+    return int(lib.dit_fuse_scale_shift(x or None, y or None, rows, hidden, rows_per_batch,
+                                        scale or None, shift or None, mod_dtype, eps, dtype,
+                                        stream or None))
+
+
+def _mod_code(t) -> int:
+    torch = _torch()
+    codes = {torch.bfloat16: QKR_BF16, torch.float16: QKR_FP16, torch.float32: QKR_FP32}
+    if t.dtype not in codes:
+        raise ValueError("scale/shift must be bfloat16, float16 or float32, got %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def fuse_scale_shift(x, scale, shift, *, out=None, eps: float = 1e-6,
+                     rows_per_batch: int | None = None, stream=None):
+    """AdaLN modulation (see ``include/fuse_scale_shift.h``); returns ``out``.
+
+    ``x``: [..., hidden] bfloat16/float16; ``scale``/``shift``: [batches, hidden]
+    (or [hidden] for one batch) of bfloat16, float16 or float32.  Row r of the
+    flattened x uses modulation row r // rows_per_batch; by default the rows
+    split evenly over the batches.  ``out`` defaults to a new tensor like x;
+    pass ``out=x`` to modulate in place.
+    """
+    torch = _torch()
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if x.numel() else 0
+    if scale.shape != shift.shape or scale.dtype != shift.dtype:
+        raise ValueError("scale and shift must match in shape and dtype")
+    if scale.shape[-1] != hidden:
+        raise ValueError("scale/shift last dimension must equal hidden")
+    batches = scale.numel() // hidden
+    if rows_per_batch is None:
+        if batches < 1 or rows % batches:
+            raise ValueError("rows do not split evenly over the modulation batches")
+        rows_per_batch = max(1, rows // batches)
+    if rows and (rows - 1) // rows_per_batch >= batches:
+        raise ValueError("scale/shift hold fewer batches than the rows need")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    if stream is None:
+        stream_ptr = torch.cuda.current_stream(x.device).cuda_stream if x.is_cuda else 0
+    elif isinstance(stream, int):
+        stream_ptr = stream
+    else:
+        stream_ptr = stream.cuda_stream
+    _check(dit_fuse_scale_shift_raw(_ptr(x), _ptr(out), rows, hidden, rows_per_batch,
+                                    _ptr(scale), _ptr(shift), _mod_code(scale), float(eps),
+                                    _x_code(x), stream_ptr))
+    return out

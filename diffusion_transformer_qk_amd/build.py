@@ -11,7 +11,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "qknorm_rope.hip")
+SRCS = [os.path.join(PKG, "csrc", "qknorm_rope.hip"),
+        os.path.join(PKG, "csrc", "fuse_scale_shift.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknorm_rope.so")
 ARCH = "gfx950"
@@ -38,7 +39,7 @@ def hipcc() -> str:
 def build(save_temps: str | None = None) -> str:
     """Build the library in-tree and return its path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
     cwd = None
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)

@@ -13,17 +13,20 @@ import pytest
 import diffusion_transformer_qk_amd as qkr
 from diffusion_transformer_qk_amd import binding as b
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "qknorm_rope.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 A = 0x10000          # a 16-byte aligned fake device address
 MIS = 0x10008        # 8-byte aligned only
 
 
 def declared_functions():
-    with open(HEADER) as f:
-        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    return set(re.findall(r"\b(qknorm_rope_\w+)\s*\(", text))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            with open(os.path.join(INCLUDE, h)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+    return names
 
 
 def test_every_declared_symbol_is_exported():
@@ -109,3 +112,57 @@ def test_python_binding_rejects_cpu_tensors():
         qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c)
     with pytest.raises(ValueError):   # wrong table size
         qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c[:3], sin=c[:3])
+
+
+# ----------------------------------------------------------------------------- AdaLN entry point
+
+
+def fss(**over):
+    args = dict(x=A, y=A + 0x100000, rows=16, hidden=6144, rows_per_batch=16, scale=A,
+                shift=A, mod_dtype=b.QKR_FP32, eps=1e-6, dtype=b.QKR_BF16, stream=0)
+    args.update(over)
+    return qkr.dit_fuse_scale_shift_raw(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(hidden=6), b.QKR_ERR_UNSUPPORTED),
+    (dict(hidden=100), b.QKR_ERR_UNSUPPORTED),
+    (dict(hidden=8200), b.QKR_ERR_UNSUPPORTED),
+    (dict(dtype=b.QKR_FP32), b.QKR_ERR_UNSUPPORTED),
+    (dict(dtype=9), b.QKR_ERR_ARG),
+    (dict(mod_dtype=3), b.QKR_ERR_ARG),
+    (dict(eps=0.0), b.QKR_ERR_ARG),
+    (dict(eps=float("nan")), b.QKR_ERR_ARG),
+    (dict(rows=-2), b.QKR_ERR_SHAPE),
+    (dict(rows=1 << 31), b.QKR_ERR_SHAPE),
+    (dict(rows_per_batch=0), b.QKR_ERR_SHAPE),
+    (dict(x=0), b.QKR_ERR_NULL),
+    (dict(y=0), b.QKR_ERR_NULL),
+    (dict(scale=0), b.QKR_ERR_NULL),
+    (dict(shift=0), b.QKR_ERR_NULL),
+    (dict(x=MIS), b.QKR_ERR_ALIGN),
+    (dict(y=A + 0x100008), b.QKR_ERR_ALIGN),
+    (dict(scale=A + 4), b.QKR_ERR_ALIGN),
+    (dict(shift=MIS), b.QKR_ERR_ALIGN),
+    (dict(y=A + 16 * 6144), b.QKR_ERR_ARG),        # y starts inside x
+    (dict(x=A + 0x100000 + 1024 * 16, y=A + 0x100000), b.QKR_ERR_ARG),   # x inside y
+])
+def test_fuse_scale_shift_rejects_before_any_hip_call(over, code):
+    assert fss(**over) == code
+
+
+def test_fuse_scale_shift_zero_rows_is_a_no_op():
+    assert fss(rows=0, x=0, y=0, scale=0, shift=0) == b.QKR_OK
+    assert fss(rows=0, hidden=12) == b.QKR_ERR_UNSUPPORTED
+
+
+def test_fuse_scale_shift_binding_checks_shapes():
+    import torch
+    x = torch.zeros(6, 64, dtype=torch.bfloat16)
+    s = torch.zeros(4, 64)
+    with pytest.raises(ValueError):      # 6 rows do not split over 4 batches
+        qkr.fuse_scale_shift(x, s, s)
+    with pytest.raises(ValueError):      # hidden mismatch
+        qkr.fuse_scale_shift(x, s[:, :32], s[:, :32])
+    with pytest.raises(ValueError):      # CPU tensors are refused
+        qkr.fuse_scale_shift(x, s[:2], s[:2])

@@ -1,0 +1,195 @@
+"""GPU parity of the AdaLN modulation (dit_fuse_scale_shift) against the fp64 oracle.
+
+Bar (no fixed tolerance is given for this step, so it follows from the
+arithmetic): every output within half an ulp of the exact value plus fp32
+noise, the noise bounded by 8e-6 times the largest term |n (1 + scale)| +
+|shift| of its row; and the output equal to the oracle's round-to-nearest-even
+image on all but <= 1e-3 of the elements.  In place and out of place must agree
+bit for bit; x (out of place), scale and shift stay unchanged; nothing outside
+y is written.
+"""
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_qk_amd as qkr
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+PAD = 4096
+CANARY = 0x6A1B
+FP32_NOISE = 8e-6
+
+
+def _decode(t, dtype):
+    bits = wl.u16(t.cpu())
+    if dtype == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _ulp(v, dtype):
+    p, emin = (11, -14) if dtype == "fp16" else (8, -126)
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
+    return 2.0 ** (e - p + 1)
+
+
+def _mod_np(t):
+    return t.numpy() if t.dtype == torch.float32 else wl.u16(t)
+
+
+def _mod_name(t):
+    return {torch.float32: "fp32", torch.bfloat16: "bf16", torch.float16: "fp16"}[t.dtype]
+
+
+def _mod_values(t):
+    return t.float().numpy().astype(np.float64)
+
+
+def oracle_rows(x, dtype, sc, sh, rows_per_batch, eps, r0=0, r1=None):
+    hidden = x.shape[-1]
+    kw = dict(hidden=hidden, rows_per_batch=rows_per_batch, mod_dtype=_mod_name(sc), eps=eps,
+              row_begin=r0, row_end=r1)
+    y = oracle.adaln(wl.u16(x), dtype, scale=_mod_np(sc), shift=_mod_np(sh), **kw)
+    z = np.zeros_like(_mod_np(sc))
+    n = oracle.adaln(wl.u16(x), dtype, scale=z, shift=z, **kw)
+    return y, n
+
+
+def check_rows(got, y, n, sc, sh, rows_per_batch, r0, dtype, what):
+    rows = y.shape[0]
+    b = (np.arange(r0, r0 + rows) // rows_per_batch)
+    scv, shv = _mod_values(sc)[b], _mod_values(sh)[b]
+    terms = np.abs(n) * np.abs(1 + scv) + np.abs(shv)
+    bound = 0.5 * _ulp(y, dtype) + FP32_NOISE * terms.max(axis=1, keepdims=True)
+    got = got.reshape(y.shape)
+    err = np.abs(got - y)
+    over = err > bound
+    assert not over.any(), "%s: %d outside the rounding model, worst excess %.3g" % (
+        what, int(over.sum()), float((err - bound).max()))
+    rne = oracle.round_to(y, dtype)
+    n_diff = int(np.count_nonzero(got != rne))
+    assert n_diff <= max(2, 1e-3 * got.size), "%s: %d of %d differ from RNE" % (what, n_diff, got.size)
+    return float(err.max())
+
+
+def guarded_empty(shape, dtype):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * PAD,), CANARY, dtype=torch.int16, device=DEV)
+    return buf[PAD:PAD + n].view(dtype).view(shape), buf
+
+
+def canaries_intact(buf):
+    return bool((buf[:PAD] == CANARY).all()) and bool((buf[-PAD:] == CANARY).all())
+
+
+def same_bits(a, b):
+    view = torch.int32 if a.dtype == torch.float32 else torch.int16
+    return a.dtype == b.dtype and torch.equal(a.view(view), b.view(view))
+
+
+def run(x, sc, sh, rows_per_batch=None, eps=wl.EPS, inplace=False):
+    xd, scd, shd = x.to(DEV), sc.to(DEV), sh.to(DEV)
+    keep = [t.clone() for t in (xd, scd, shd)]
+    if inplace:
+        out = qkr.fuse_scale_shift(xd, scd, shd, out=xd, eps=eps, rows_per_batch=rows_per_batch)
+        torch.cuda.synchronize()
+        assert same_bits(scd, keep[1]) and same_bits(shd, keep[2])
+        return out.cpu()
+    y, buf = guarded_empty(x.shape, x.dtype)
+    qkr.fuse_scale_shift(xd, scd, shd, out=y, eps=eps, rows_per_batch=rows_per_batch)
+    torch.cuda.synchronize()
+    assert canaries_intact(buf), "write outside y"
+    for a, b in zip(keep, (xd, scd, shd)):
+        assert same_bits(a, b), "input changed"
+    return y.cpu()
+
+
+@pytest.mark.parametrize("dtype,mod", [("bf16", "fp32"), ("bf16", "bf16"), ("fp16", "fp32"),
+                                       ("fp16", "fp16"), ("bf16", "fp16")])
+def test_flux_shape_full(dtype, mod):
+    w = wl.ADALN_WORKLOADS["adaln_flux"]
+    x, sc, sh = wl.adaln_inputs(w.seed, w.rows, w.hidden, w.batches, dtype, mod)
+    out = run(x, sc, sh)
+    y, n = oracle_rows(x, dtype, sc, sh, w.rows_per_batch, wl.EPS)
+    m = check_rows(_decode(out, dtype), y, n, sc, sh, w.rows_per_batch, 0, dtype, "flux")
+    print("flux", dtype, mod, "max_abs", m, "max|y|", np.abs(y).max())
+
+
+def _windows(rows, rng, n=10, width=40, extra=()):
+    starts = sorted(set(rng.integers(0, rows - width, n).tolist()) | set(extra))
+    return [(0, width)] + [(s, s + width) for s in starts] + [(rows - width, rows)]
+
+
+@pytest.mark.parametrize("key", ["adaln_wan", "adaln_wan_cfg2"])
+def test_wan_shapes_sampled(key):
+    w = wl.ADALN_WORKLOADS[key]
+    x, sc, sh = wl.adaln_inputs(w.seed, w.rows, w.hidden, w.batches, "bf16", "fp32")
+    out = run(x, sc, sh)
+    rng = np.random.default_rng(w.seed)
+    boundary = [w.rows_per_batch - 20] if w.batches > 1 else []
+    worst = 0.0
+    for a, b in _windows(w.rows, rng, extra=boundary):
+        y, n = oracle_rows(x, "bf16", sc, sh, w.rows_per_batch, wl.EPS, a, b)
+        worst = max(worst, check_rows(_decode(out[a:b], "bf16"), y, n, sc, sh, w.rows_per_batch,
+                                      a, "bf16", "%s rows %d:%d" % (key, a, b)))
+    print(key, "sampled max_abs", worst)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_in_place_equals_out_of_place(dtype):
+    x, sc, sh = wl.adaln_inputs(77, 300, 5120, 3, dtype, "bf16")
+    a = run(x, sc, sh)
+    b = run(x, sc, sh, inplace=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("rows,hidden,rpb,batches", [
+    (1, 8, 1, 1), (3, 64, 1, 3), (257, 1000, 100, 3), (65, 2048, 13, 5), (17, 6152, 4, 5),
+    (9, 8192, 9, 1), (40, 24, 7, 6), (128, 3072, 64, 2), (5, 2056, 2, 3)])
+@pytest.mark.parametrize("dtype,mod", [("bf16", "fp32"), ("fp16", "bf16")])
+def test_ragged_widths_and_batches(rows, hidden, rpb, batches, dtype, mod):
+    x, sc, sh = wl.adaln_inputs(rows * 7 + hidden, rows, hidden, batches, dtype, mod)
+    out = run(x, sc, sh, rows_per_batch=rpb)
+    y, n = oracle_rows(x, dtype, sc, sh, rpb, wl.EPS)
+    check_rows(_decode(out, dtype), y, n, sc, sh, rpb, 0, dtype, "ragged")
+
+
+def test_constant_rows_and_large_eps():
+    rows, hidden = 6, 512
+    x = torch.full((rows, hidden), 3.25, dtype=torch.bfloat16)
+    x[3] = torch.linspace(-4, 4, hidden).to(torch.bfloat16)
+    sc = torch.randn(1, hidden, generator=torch.Generator().manual_seed(3)) * 0.5
+    sh = torch.randn(1, hidden, generator=torch.Generator().manual_seed(4)) * 0.5
+    for eps in (1e-6, 0.5):
+        out = run(x, sc, sh, eps=eps)
+        y, n = oracle_rows(x, "bf16", sc, sh, rows, eps)
+        check_rows(_decode(out, "bf16"), y, n, sc, sh, rows, 0, "bf16", "constant eps=%g" % eps)
+        # a constant row normalises to zero: its output is the shift, rounded once
+        assert np.array_equal(_decode(out[0], "bf16"), oracle.round_to(_mod_values(sh)[0], "bf16"))
+
+
+def test_zero_rows_is_a_no_op():
+    x = torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV)
+    s = torch.zeros(1, 64, device=DEV)
+    out = qkr.fuse_scale_shift(x, s, s, rows_per_batch=1)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def test_partial_overlap_and_misalignment_are_rejected():
+    rows, hidden = 8, 64
+    buf = torch.zeros(2 * rows * hidden + 8, dtype=torch.bfloat16, device=DEV)
+    x = buf[:rows * hidden].view(rows, hidden)
+    y = buf[hidden:hidden + rows * hidden].view(rows, hidden)        # overlaps x by 7 rows
+    s = torch.zeros(1, hidden, device=DEV)
+    with pytest.raises(qkr.QkrError) as e:
+        qkr.fuse_scale_shift(x, s, s, out=y)
+    assert e.value.status == qkr.binding.QKR_ERR_ARG
+    xm = buf[1:1 + rows * hidden].view(rows, hidden)                 # 2-byte offset
+    with pytest.raises(qkr.QkrError) as e:
+        qkr.fuse_scale_shift(xm, s, s)
+    assert e.value.status == qkr.binding.QKR_ERR_ALIGN
