@@ -37,13 +37,18 @@ if ROOT not in sys.path:
 
 METRIC = "QK-norm+RoPE µs/call and achieved HBM GB/s (% of peak), Wan 40×128 shape"
 PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
-KERNEL_SRC = os.path.join(ROOT, "diffusion_transformer_qk_amd", "csrc", "qknorm_rope.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "diffusion_transformer_qk_amd", "csrc", name)
+               for name in ("qknorm_rope.hip", "device_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 (16 hex) over the QK-norm + RoPE kernel's sources, in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, layout: str, style: str):

@@ -1,0 +1,31 @@
+"""bench.py pieces that need no GPU: the one-GPU refusal and the traffic record."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "4"],
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 2
+    assert "one GPU" in out.stderr
+
+
+def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
+    rec = {"kernel_source_sha256_16": bench.kernel_source_hash(),
+           "runs": {"headline/shared/interleaved": {"bytes_per_launch": 123}}}
+    path = os.path.join(tmp_path, "t.json")
+    with open(path, "w") as f:
+        json.dump(rec, f)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
+    assert bench.measured_traffic("headline", "shared", "interleaved") == 123
+    assert bench.measured_traffic("headline", "per_head", "interleaved") is None
+    rec["kernel_source_sha256_16"] = "0" * 16
+    with open(path, "w") as f:
+        json.dump(rec, f)
+    assert bench.measured_traffic("headline", "shared", "interleaved") is None
