@@ -1,5 +1,5 @@
-"""CPU oracle for the fused QK-norm + RoPE pass and the adaptive layer norm
-with scale/shift: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the fused QK-norm + RoPE pass, the adaptive layer norm with
+scale/shift and the group norm followed by SiLU: TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -77,6 +77,9 @@ class Oracle:
         lib.qkr_oracle_adaln.argtypes = [p, c_int, i64, i64, i64, i64, p, p, c_int,
                                          ctypes.c_float, p]
         lib.qkr_oracle_adaln.restype = c_int
+        lib.qkr_oracle_group_norm_silu.argtypes = [p, c_int, i64, i64, i64, i64, i64, p, p,
+                                                   c_int, ctypes.c_float, p]
+        lib.qkr_oracle_group_norm_silu.restype = c_int
         lib.qkr_oracle_max_threads.argtypes = []
         lib.qkr_oracle_max_threads.restype = c_int
         self.lib = lib
@@ -167,6 +170,38 @@ class Oracle:
             raise ValueError("oracle rejected its arguments")
         return out
 
+    def group_norm_silu(self, x_bits: np.ndarray, x_dtype: str, *, channels: int, spatial: int,
+                        groups: int, gamma, beta, param_dtype: str, eps: float,
+                        group_begin: int = 0, group_end: int | None = None,
+                        out: np.ndarray | None = None) -> np.ndarray:
+        """fp64 [(group_end - group_begin) * (channels // groups) * spatial] output.
+
+        ``x_bits``: the whole [n, channels, spatial] tensor's uint16 storage;
+        groups are the n*groups (sample, group) pairs in memory order.
+        ``gamma``/``beta``: [channels] float32 ("fp32") or uint16 patterns.
+        """
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16).reshape(-1)
+        gsize = channels // groups * spatial
+        total = x.size // gsize
+        assert x.size == total * gsize and channels % groups == 0
+        if group_end is None:
+            group_end = total
+        assert 0 <= group_begin <= group_end <= total
+        want = np.float32 if param_dtype == "fp32" else np.uint16
+        g = np.ascontiguousarray(gamma)
+        b = np.ascontiguousarray(beta)
+        assert g.dtype == want and b.dtype == want and g.size == channels == b.size
+        n = (group_end - group_begin) * gsize
+        if out is None:
+            out = np.empty(n, dtype=np.float64)
+        assert out.size == n and out.dtype == np.float64 and out.flags.c_contiguous
+        rc = self.lib.qkr_oracle_group_norm_silu(
+            _ptr(x), DTYPE_CODE[x_dtype], channels, spatial, groups, group_begin, group_end,
+            _ptr(g), _ptr(b), DTYPE_CODE[param_dtype], ctypes.c_float(eps), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return out
+
     def fused_qk(self, qkv_bits: np.ndarray, x_dtype: str, *, heads: int, head_dim: int,
                  q_gamma, k_gamma, eps: float, cos, sin, cos_dtype="fp32",
                  cos_layout="shared", style="interleaved", t_begin=0, t_end=None):
@@ -214,3 +249,7 @@ def fused_qk(qkv_bits, x_dtype, **kw):
 
 def adaln(x_bits, x_dtype, **kw):
     return default().adaln(x_bits, x_dtype, **kw)
+
+
+def group_norm_silu(x_bits, x_dtype, **kw):
+    return default().group_norm_silu(x_bits, x_dtype, **kw)

@@ -31,8 +31,9 @@
  * gamma multiplied directly and before RoPE, the +angle sign, no intermediate
  * rounding) are the plain RMSNorm / RoPE definitions.
  *
- * The file also holds the oracle of the adaptive layer norm with scale and
- * shift (qkr_oracle_adaln, below).
+ * The file also holds the oracles of the adaptive layer norm with scale and
+ * shift (qkr_oracle_adaln) and of the group norm followed by SiLU
+ * (qkr_oracle_group_norm_silu), below.
  *
  * Every function here is pinned by CPU tests against brute force in exact
  * arithmetic, closed forms, invariants and library routines.
@@ -259,6 +260,65 @@ int qkr_oracle_adaln(const uint16_t* x, int x_dtype, int64_t row_begin, int64_t 
             const double n = (decode16(xr[c], x_dtype) - mean) * inv;
             yr[c] = n * (1.0 + mod_value(scale, mod_dtype, b * C + c))
                     + mod_value(shift, mod_dtype, b * C + c);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Group norm followed by SiLU: the "group_norm_silu" (VAE) step that
+ * TensorRT-Model-Connect PR "perf(diffusion): fused qknorm rope Flux 2.0"
+ * lists among its follow-ups.  The page gives only the name; this is the
+ * plain definition (group normalisation with a per-channel affine, then
+ * SiLU(y) = y / (1 + exp(-y))):
+ *
+ *   x [n, C, S] contiguous, G groups of Cg = C / G channels; for sample i
+ *   and group g, over the Cg * S elements of channels g*Cg .. g*Cg + Cg - 1:
+ *     mean = (1/(Cg S)) sum x;  var = (1/(Cg S)) sum (x - mean)^2   (biased)
+ *     y    = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c]
+ *     out  = y / (1 + exp(-y))
+ *
+ * x: 16-bit (x_dtype 0 bf16, 1 fp16); gamma, beta: [C] of param_dtype
+ * (0 bf16, 1 fp16, 2 fp32).  out: fp64 [n, C, S] for the groups
+ * [group_begin, group_end) of the n*G (sample, group) pairs, in order.
+ */
+int qkr_oracle_group_norm_silu(const uint16_t* x, int x_dtype, int64_t channels, int64_t spatial,
+                               int64_t groups, int64_t group_begin, int64_t group_end,
+                               const void* gamma, const void* beta, int param_dtype, float eps,
+                               double* out)
+{
+    if (channels <= 0 || spatial <= 0 || groups <= 0 || channels % groups)
+        return -1;
+    if (group_begin < 0 || group_end < group_begin)
+        return -1;
+    if (param_dtype != QKR_O_BF16 && param_dtype != QKR_O_FP16 && param_dtype != QKR_O_FP32)
+        return -1;
+    const int64_t cg = channels / groups;
+    const int64_t gsize = cg * spatial;
+    const double eps64 = (double)eps;
+
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t q = group_begin; q < group_end; ++q) {
+        /* (sample, group) pair q covers one contiguous run of gsize elements */
+        const uint16_t* xq = x + q * gsize;
+        double* oq = out + (q - group_begin) * gsize;
+        const int64_t c0 = (q % groups) * cg;
+
+        double sum = 0.0;
+        for (int64_t e = 0; e < gsize; ++e)
+            sum += decode16(xq[e], x_dtype);
+        const double mean = sum / (double)gsize;
+        double sum_dev = 0.0;
+        for (int64_t e = 0; e < gsize; ++e) {
+            const double dev = decode16(xq[e], x_dtype) - mean;
+            sum_dev += dev * dev;
+        }
+        const double inv = 1.0 / sqrt(sum_dev / (double)gsize + eps64);
+        for (int64_t e = 0; e < gsize; ++e) {
+            const int64_t c = c0 + e / spatial;
+            const double y = (decode16(xq[e], x_dtype) - mean) * inv * mod_value(gamma, param_dtype, c)
+                             + mod_value(beta, param_dtype, c);
+            oq[e] = y / (1.0 + exp(-y));
         }
     }
     return 0;

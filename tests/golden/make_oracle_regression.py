@@ -18,6 +18,7 @@ import oracle  # noqa: E402
 import workloads as wl  # noqa: E402
 
 ADALN_CASES = [("bf16", "fp32"), ("fp16", "bf16")]
+GN_CASES = [("bf16", "fp32"), ("fp16", "fp16")]
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_regression.txt")
 CASES = [  # (style, x dtype, cos dtype, cos layout, head_dim)
     ("interleaved", "bf16", "fp32", "shared", 64),
@@ -45,6 +46,12 @@ def cases():
         y = oracle.adaln(wl.u16(x), xdt, hidden=200, rows_per_batch=3, scale=to_np(sc),
                          shift=to_np(sh), mod_dtype=mdt, eps=wl.EPS)
         yield "adaln %s %s" % (xdt, mdt), y.ravel()
+    for xdt, pdt in GN_CASES:
+        x, g, b = wl.gn_inputs(4344, 2, 16, 48, xdt, pdt)
+        to_np = (lambda t: t.numpy()) if pdt == "fp32" else wl.u16
+        y = oracle.group_norm_silu(wl.u16(x), xdt, channels=16, spatial=48, groups=4,
+                                   gamma=to_np(g), beta=to_np(b), param_dtype=pdt, eps=wl.EPS)
+        yield "group_norm_silu %s %s" % (xdt, pdt), y
 
 
 def main():

@@ -26,7 +26,7 @@ def _read():
 
 def test_oracle_matches_regression_lock():
     stored = _read()
-    assert len(stored) == len(gen.CASES) + len(gen.ADALN_CASES)
+    assert len(stored) == len(gen.CASES) + len(gen.ADALN_CASES) + len(gen.GN_CASES)
     for name, vals in gen.cases():
         for i, v in stored[name].items():
             assert vals[i] == v, (name, i)

@@ -138,3 +138,62 @@ def test_adaln_mutation_is_caught(tmp_path, name):
         f.write(src.replace(old, new, 1))
     lib = oracle.compile_source(path, os.path.join(tmp_path, "libmut.so"))
     assert _caught_adaln(oracle.Oracle(lib)), "no pin catches mutation " + name
+
+
+# ----------------------------------------------------------------------------- group norm + SiLU
+
+import tests.test_oracle_gn_pins as gn_pins  # noqa: E402
+
+GN_MUTATIONS = {
+    "gn_unbiased_variance": ("sqrt(sum_dev / (double)gsize + eps64)",
+                             "sqrt(sum_dev / (double)(gsize - 1) + eps64)"),
+    "gn_eps_outside_root": ("sqrt(sum_dev / (double)gsize + eps64)",
+                            "sqrt(sum_dev / (double)gsize) + eps64"),
+    "gn_channel_shifted": ("const int64_t c = c0 + e / spatial;",
+                           "const int64_t c = c0 + (e / spatial + 1) % cg;"),
+    "gn_group_rotated": ("const int64_t c0 = (q % groups) * cg;",
+                         "const int64_t c0 = ((q + 1) % groups) * cg;"),
+    "gn_silu_sign": ("oq[e] = y / (1.0 + exp(-y));", "oq[e] = y / (1.0 + exp(y));"),
+    "gn_no_beta": ("+ mod_value(beta, param_dtype, c);", "+ 0.0;"),
+    "gn_gamma_read_from_beta": ("* inv * mod_value(gamma, param_dtype, c)",
+                                "* inv * mod_value(beta, param_dtype, c)"),
+    "gn_mean_drops_last": ("for (int64_t e = 0; e < gsize; ++e)\n            sum += ",
+                           "for (int64_t e = 0; e + 1 < gsize; ++e)\n            sum += "),
+}
+
+GN_PIN_TESTS = [
+    (gn_pins.test_matches_torch_group_norm_silu, {"groups": 4, "x_dtype": "bf16",
+                                                   "param_dtype": "fp32"}),
+    (gn_pins.test_instance_norm_special_case, {}),
+    (gn_pins.test_zero_gamma_and_constant_groups_give_silu_of_beta, {}),
+    (gn_pins.test_silu_odd_part_identity, {}),
+    (gn_pins.test_brute_force, {"x_dtype": "fp16", "param_dtype": "fp16"}),
+]
+
+
+def _caught_gn(variant) -> list:
+    caught = []
+    for fn, kw in GN_PIN_TESTS:
+        try:
+            with np.errstate(all="ignore"):
+                fn(variant, **kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+    return caught
+
+
+def test_unmutated_source_passes_every_gn_pin():
+    assert _caught_gn(oracle.default()) == []
+
+
+@pytest.mark.parametrize("name", sorted(GN_MUTATIONS))
+def test_gn_mutation_is_caught(tmp_path, name):
+    old, new = GN_MUTATIONS[name]
+    with open(oracle.SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
+    path = os.path.join(tmp_path, "mut.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new, 1))
+    lib = oracle.compile_source(path, os.path.join(tmp_path, "libmut.so"))
+    assert _caught_gn(oracle.Oracle(lib)), "no pin catches mutation " + name

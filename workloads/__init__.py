@@ -288,3 +288,80 @@ def adaln_inputs(seed: int, rows: int, hidden: int, batches: int, dtype: str = "
 def adaln_bytes(rows: int, hidden: int, batches: int, x_bytes: int = 2, mod_bytes: int = 4) -> int:
     """Bytes the pass must move: x read, y written, scale and shift read once."""
     return rows * hidden * x_bytes * 2 + batches * hidden * mod_bytes * 2
+
+
+# ----------------------------------------------------------------------------- group norm + SiLU
+#
+# Inputs for the VAE group norm + SiLU step: x [n, C, S] (S = H*W), each
+# channel c = N(0,1) * a_c + b_c with a_c = exp(U[ln 0.2, ln 5]) and
+# b_c = N(0, 1), fp32 then one RNE cast; gamma = 1 + 0.1 N(0,1),
+# beta = 0.1 N(0,1) per channel.  Seeds: SeedSequence(seed) spawned into
+# channel scale, channel offset, activations (per block of 2^20 elements),
+# gamma, beta.
+
+
+@dataclass(frozen=True)
+class GroupNormWorkload:
+    key: str
+    seed: int
+    n: int
+    channels: int
+    height: int
+    width: int
+    groups: int
+    dtypes: tuple
+    note: str = field(default="", compare=False)
+
+    @property
+    def spatial(self) -> int:
+        return self.height * self.width
+
+
+GN_WORKLOADS = {
+    "gn_vae_mid": GroupNormWorkload("gn_vae_mid", 1201, 1, 512, 128, 128, 32, ("bf16",),
+                                    note="VAE decoder mid block at 1/8 of 1024x1024"),
+    "gn_vae_up": GroupNormWorkload("gn_vae_up", 1202, 1, 256, 512, 512, 32, ("bf16", "fp16"),
+                                   note="VAE decoder up block at 1/2 resolution"),
+    "gn_vae_out": GroupNormWorkload("gn_vae_out", 1203, 1, 128, 1024, 1024, 32, ("bf16",),
+                                    note="VAE decoder last block at 1024x1024"),
+}
+
+GN_BLOCK = 1 << 20
+
+
+def gn_inputs(seed: int, n: int, channels: int, spatial: int, dtype: str = "bf16",
+              param_dtype: str = "fp32"):
+    """(x [n, channels, spatial], gamma [channels], beta [channels]) CPU tensors."""
+    kids = np.random.SeedSequence(seed).spawn(5)
+    ga = np.random.Generator(np.random.PCG64(kids[0]))
+    a = np.exp(ga.uniform(math.log(0.2), math.log(5.0), size=channels)).astype(np.float32)
+    gb = np.random.Generator(np.random.PCG64(kids[1]))
+    b = gb.standard_normal(channels).astype(np.float32)
+    total = n * channels * spatial
+    out = np.empty(total, dtype=np.float32)
+    n_blocks = -(-total // GN_BLOCK) if total else 0
+    blocks = kids[2].spawn(n_blocks) if n_blocks else []
+
+    def work(k):
+        lo, hi = k * GN_BLOCK, min(total, (k + 1) * GN_BLOCK)
+        g = np.random.Generator(np.random.PCG64(blocks[k]))
+        g.standard_normal(hi - lo, dtype=np.float32, out=out[lo:hi])
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(n_blocks)))
+    v = out.reshape(n, channels, spatial)
+    v *= a[None, :, None]
+    v += b[None, :, None]
+    x = _cast(v, dtype)
+    params = []
+    for child, base in ((kids[3], 1.0), (kids[4], 0.0)):
+        g = np.random.Generator(np.random.PCG64(child))
+        p = (base + 0.1 * g.standard_normal(channels)).astype(np.float32)
+        t = torch.from_numpy(p)
+        params.append(t if param_dtype == "fp32" else t.to(DTYPES[param_dtype]))
+    return x, params[0], params[1]
+
+
+def gn_bytes(n: int, channels: int, spatial: int, x_bytes: int = 2, param_bytes: int = 4) -> int:
+    """Bytes the step must move: x read, y written, gamma and beta read once."""
+    return n * channels * spatial * x_bytes * 2 + channels * param_bytes * 2
