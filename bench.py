@@ -13,6 +13,8 @@ oracle on a bounded sample of the same workload.
 
   python bench.py --op fuse_scale_shift [--workload adaln_wan|adaln_flux|adaln_wan_cfg2]
                   [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
+  python bench.py --op group_norm_silu [--workload gn_vae_out|gn_vae_up|gn_vae_mid]
+                  [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                   [--layout shared|per_head] [--style interleaved|rotate_half]
                   [--dtype bf16|fp16] [--flush] [--no-cpu-baseline] [--calib-copy]
@@ -70,7 +72,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--op", default="qknorm_rope", choices=["qknorm_rope", "fuse_scale_shift"])
+    ap.add_argument("--op", default="qknorm_rope",
+                    choices=["qknorm_rope", "fuse_scale_shift", "group_norm_silu"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mod-dtype", default="fp32", choices=["fp32", "bf16", "fp16"])
     ap.add_argument("--inplace", action="store_true", help="AdaLN: write y over x")
@@ -221,6 +224,60 @@ def bench_fuse_scale_shift(args):
     return 0
 
 
+def bench_group_norm_silu(args):
+    """Group norm + SiLU on one of the GN_WORKLOADS; prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_qk_amd as qkr
+    import workloads as wl
+    w = wl.GN_WORKLOADS[args.workload or "gn_vae_out"]
+    dtype = args.dtype or w.dtypes[0]
+    dev = torch.device("cuda:0")
+    x_cpu, g, b = wl.gn_inputs(w.seed, w.n, w.channels, w.spatial, dtype, args.mod_dtype)
+    x = x_cpu.to(dev).view(w.n, w.channels, w.height, w.width)
+    gd, bd = g.to(dev), b.to(dev)
+    y = x if args.inplace else torch.empty_like(x)
+    need = qkr.group_norm_silu_workspace_size(w.n, w.channels, w.spatial, w.groups)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    pbytes = 4 if args.mod_dtype == "fp32" else 2
+    nbytes = wl.gn_bytes(w.n, w.channels, w.spatial, param_bytes=pbytes)
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+
+    def launch():
+        qkr.group_norm_silu(x, gd, bd, w.groups, out=y, eps=wl.EPS, workspace=ws, stream=handle)
+
+    per, region_ms, wall = time_launches(launch, stream, args.steps, args.warmup, flush_buf)
+    K = args.steps
+    mean_us = float(per.mean())
+    achieved = nbytes / (mean_us * 1e-6) / 1e9
+    value = achieved if args.flush else nbytes * K / (region_ms * 1e-3) / 1e9
+    result = {
+        "metric": "group_norm_silu µs/call and achieved HBM GB/s (% of peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(region_ms / K, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": "%s: x %s [%d, %d, %d, %d], %d groups, %s affine%s%s"
+                               % (w.key, dtype, w.n, w.channels, w.height, w.width, w.groups,
+                                  args.mod_dtype, ", in place" if args.inplace else "",
+                                  ", cache flushed" if args.flush else ""),
+                   "n": w.n, "channels": w.channels, "spatial": w.spatial, "groups": w.groups,
+                   "workspace_bytes": need, "math": "f32", "parallelism": "single GPU"},
+        "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
+                        "p10": round(float(np.percentile(per, 10)), 2),
+                        "p90": round(float(np.percentile(per, 90)), 2)},
+        "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
+        "bytes_per_call": nbytes, "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None},
+    }
+    print(json.dumps(result))
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -240,6 +297,8 @@ def main():
     qkr.load_library()
     if args.op == "fuse_scale_shift":
         return bench_fuse_scale_shift(args)
+    if args.op == "group_norm_silu":
+        return bench_group_norm_silu(args)
     args.workload = args.workload or "headline"
     w = wl.WORKLOADS[args.workload]
     style = args.style or w.styles[0]

@@ -1,8 +1,9 @@
 """ctypes binding of ``libqknorm_rope.so`` (argument marshalling only).
 
 Every step runs in the HIP kernels behind the C ABI declared in
-``include/qknorm_rope.h`` (fused QK-norm + RoPE) and
-``include/fuse_scale_shift.h`` (AdaLN modulation); this module turns torch
+``include/qknorm_rope.h`` (fused QK-norm + RoPE), ``include/fuse_scale_shift.h``
+(AdaLN modulation) and ``include/group_norm_silu.h`` (group norm + SiLU);
+this module turns torch
 tensors into device pointers, sizes and enum codes and raises on a non-zero
 status.  There is no fallback: if the library is missing, loading fails
 loudly.
@@ -18,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libqknorm_rope.so")
 QKR_OK = 0
 QKR_ERR_NULL, QKR_ERR_SHAPE, QKR_ERR_ALIGN = -1, -2, -3
 QKR_ERR_UNSUPPORTED, QKR_ERR_MODE, QKR_ERR_HIP, QKR_ERR_ARG = -4, -5, -6, -7
+QKR_ERR_WORKSPACE = -8
 QKR_BF16, QKR_FP16, QKR_FP32 = 0, 1, 2
 QKR_COS_SHARED, QKR_COS_PER_HEAD = 0, 1
 QKR_ROPE_INTERLEAVED, QKR_ROPE_ROTATE_HALF = 0, 1
@@ -25,7 +27,8 @@ QKR_ROPE_INTERLEAVED, QKR_ROPE_ROTATE_HALF = 0, 1
 LAYOUTS = {"shared": QKR_COS_SHARED, "per_head": QKR_COS_PER_HEAD}
 STYLES = {"interleaved": QKR_ROPE_INTERLEAVED, "rotate_half": QKR_ROPE_ROTATE_HALF}
 EXPORTS = ("qknorm_rope_fused", "qknorm_rope_strerror", "qknorm_rope_version",
-           "qknorm_rope_kernel_info", "dit_fuse_scale_shift")
+           "qknorm_rope_kernel_info", "dit_fuse_scale_shift",
+           "dit_group_norm_silu_workspace_size", "dit_group_norm_silu")
 MOD_DTYPES = {"bf16": QKR_BF16, "fp16": QKR_FP16, "fp32": QKR_FP32}
 
 
@@ -70,6 +73,11 @@ def load_library(path: str = LIB_PATH):
     lib.qknorm_rope_kernel_info.restype = ctypes.c_int
     lib.dit_fuse_scale_shift.argtypes = [vp, vp, i64, i32, i64, vp, vp, i32, f32, i32, vp]
     lib.dit_fuse_scale_shift.restype = ctypes.c_int
+    lib.dit_group_norm_silu_workspace_size.argtypes = [i64, i32, i64, i32]
+    lib.dit_group_norm_silu_workspace_size.restype = i64
+    lib.dit_group_norm_silu.argtypes = [vp, vp, i64, i32, i64, i32, vp, vp, i32, f32, i32, vp, i64,
+                                        vp]
+    lib.dit_group_norm_silu.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -260,4 +268,61 @@ def fuse_scale_shift(x, scale, shift, *, out=None, eps: float = 1e-6,
     _check(dit_fuse_scale_shift_raw(_ptr(x), _ptr(out), rows, hidden, rows_per_batch,
                                     _ptr(scale), _ptr(shift), _mod_code(scale), float(eps),
                                     _x_code(x), stream_ptr))
+    return out
+
+
+def group_norm_silu_workspace_size(n: int, channels: int, spatial: int, groups: int) -> int:
+    """Workspace bytes the call needs (negative: a QKR_ERR_* code for bad sizes)."""
+    return int(load_library().dit_group_norm_silu_workspace_size(n, channels, spatial, groups))
+
+
+def dit_group_norm_silu_raw(x: int, y: int, n: int, channels: int, spatial: int, groups: int,
+                            gamma: int, beta: int, param_dtype: int, eps: float, dtype: int,
+                            workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The group-norm C entry point with integer pointers; returns the raw status."""
+    lib = load_library()
+    return int(lib.dit_group_norm_silu(x or None, y or None, n, channels, spatial, groups,
+                                       gamma or None, beta or None, param_dtype, eps, dtype,
+                                       workspace or None, workspace_bytes, stream or None))
+
+
+def group_norm_silu(x, gamma, beta, groups: int, *, out=None, eps: float = 1e-6,
+                    workspace=None, stream=None):
+    """Group norm + affine + SiLU (see ``include/group_norm_silu.h``); returns ``out``.
+
+    ``x``: [n, channels, *spatial] bfloat16/float16 (spatial dims flattened,
+    their product a multiple of 8).  ``gamma``/``beta``: [channels].
+    ``workspace``: a device tensor of at least the queried size; when None and
+    one is needed, a byte tensor is allocated here with torch (the library
+    itself never allocates).  ``out`` defaults to a new tensor; ``out=x``
+    works in place.
+    """
+    torch = _torch()
+    if x.dim() < 3:
+        raise ValueError("x must be [n, channels, *spatial]")
+    n, channels = x.shape[0], x.shape[1]
+    spatial = 1
+    for d in x.shape[2:]:
+        spatial *= d
+    if gamma.shape != (channels,) or beta.shape != (channels,) or gamma.dtype != beta.dtype:
+        raise ValueError("gamma and beta must be [channels] of one dtype")
+    need = group_norm_silu_workspace_size(n, channels, spatial, groups) if x.numel() else 0
+    if need < 0:
+        raise QkrError(need, strerror(need))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    if stream is None:
+        stream_ptr = torch.cuda.current_stream(x.device).cuda_stream if x.is_cuda else 0
+    elif isinstance(stream, int):
+        stream_ptr = stream
+    else:
+        stream_ptr = stream.cuda_stream
+    _check(dit_group_norm_silu_raw(_ptr(x), _ptr(out), n, channels, spatial, groups, _ptr(gamma),
+                                   _ptr(beta), _mod_code(gamma), float(eps), _x_code(x),
+                                   _ptr(workspace), ws_bytes, stream_ptr))
     return out

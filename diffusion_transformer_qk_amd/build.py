@@ -12,7 +12,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", "qknorm_rope.hip"),
-        os.path.join(PKG, "csrc", "fuse_scale_shift.hip")]
+        os.path.join(PKG, "csrc", "fuse_scale_shift.hip"),
+        os.path.join(PKG, "csrc", "group_norm_silu.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknorm_rope.so")
 ARCH = "gfx950"

@@ -91,6 +91,36 @@ __device__ __forceinline__ void load_f32x8(const float* p, float f[8])
     }
 }
 
+// Sum over all 64 lanes of a wave; every lane ends with the same value.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<0xB1>(v);      // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);      // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);     // row_half_mirror
+    v += dpp<0x140>(v);     // row_mirror: 16-lane row total in every lane
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Sum over a workgroup of WAVES waves through `slot` (WAVES floats of LDS),
+// added in wave order by every thread, so all threads get identical bits.
+// Contains one barrier; a slot may be reused once every thread has passed a
+// later barrier.
+template <int WAVES>
+__device__ __forceinline__ float block_sum(float v, float* slot)
+{
+    v = wave_sum(v);
+    if (threadIdx.x % kWave == 0)
+        slot[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float t = slot[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w)
+        t += slot[w];
+    return t;
+}
+
 // Logical block of hardware block `bid`.  The dispatcher deals consecutive
 // hardware blocks to consecutive dies; ORDER < 0 remaps that so each die
 // walks one contiguous run of blocks (die d gets the d-th eighth of the grid,

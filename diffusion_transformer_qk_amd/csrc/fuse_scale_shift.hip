@@ -50,33 +50,6 @@ struct FssParams {
     float eps;
 };
 
-// Sum over all 64 lanes of a wave; every lane ends with the same value.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v += dpp<0xB1>(v);      // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);      // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);     // row_half_mirror
-    v += dpp<0x140>(v);     // row_mirror: 16-lane row total in every lane
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-
-// Sum over the workgroup through `slot` (kWaves floats of LDS), added in wave
-// order by every thread, so all threads get identical bits.
-__device__ __forceinline__ float block_sum(float v, float* slot)
-{
-    v = wave_sum(v);
-    if (threadIdx.x % kWave == 0)
-        slot[threadIdx.x / kWave] = v;
-    __syncthreads();
-    float t = slot[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        t += slot[w];
-    return t;
-}
-
 template <int MOD>
 constexpr int mod_vecs() { return MOD == QKR_FP32 ? 2 : 1; }   // 16-byte vectors per 8 entries
 
@@ -163,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void fuse_scale_shift_kernel(const FssParam
             for (int k = 0; k < 8; ++k)
                 sum += f[k];
         }
-        const float mean = block_sum(sum, red[0]) / (float)C;
+        const float mean = block_sum<kWaves>(sum, red[0]) / (float)C;
 
         // pass 2: biased variance from the deviations
         float ss = 0.0f;
@@ -179,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void fuse_scale_shift_kernel(const FssParam
                 }
             }
         }
-        const float rstd = __builtin_amdgcn_rsqf(block_sum(ss, red[1]) / (float)C + p.eps);
+        const float rstd = __builtin_amdgcn_rsqf(block_sum<kWaves>(ss, red[1]) / (float)C + p.eps);
 
         // the row's batch (uniform over the workgroup): reload its modulation
         const int64_t b = r / p.rows_per_batch;

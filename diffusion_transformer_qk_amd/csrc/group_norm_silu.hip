@@ -1,0 +1,336 @@
+// group_norm_silu.hip -- fused group norm + per-channel affine + SiLU for
+// gfx950 (the VAE step; definition in include/group_norm_silu.h).
+//
+// A group (Cg channels x spatial elements of one sample) is one contiguous
+// run of memory.  Work is cut into chunks of kChunk elements, one 256-thread
+// workgroup per (group, chunk), each thread holding kVpt 16-byte vectors:
+//   * one chunk per group: a single kernel keeps the chunk in registers,
+//     reduces mean and biased variance in two passes and writes y (one read,
+//     one write);
+//   * several chunks: gn_stats_kernel reduces each chunk to (mean, sum of
+//     squared deviations) in the workspace, then gn_apply_kernel combines
+//     the group's partials with the pairwise update (sum n_i m_i / N, then
+//     sum M2_i + n_i (m_i - m)^2) in a fixed order, so every workgroup of a
+//     group gets the same statistics, and writes y for its chunk.  The host
+//     runs the two kernels over slabs of groups small enough for the slab to
+//     stay in the 256 MB Infinity Cache between them: the stats pass reads
+//     with ordinary loads, the apply pass re-reads with non-temporal loads
+//     and writes non-temporally.
+// Per vector of 8 elements (spatial is a multiple of 8, so a vector never
+// straddles channels): t = fma((x - mean) * rstd, gamma[c], beta[c]),
+// y = t / (1 + exp(-t)), packed with round-to-nearest-even.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "group_norm_silu.h"
+
+namespace {
+
+using namespace qkr_dev;
+
+constexpr int kWaves = 4;
+constexpr int kBlock = kWaves * kWave;
+constexpr int kVpt = 8;                                   // vectors per thread per chunk
+constexpr int64_t kChunk = (int64_t)kBlock * kVpt * kVec; // 16384 elements
+constexpr int64_t kSlabBytes = 96ll << 20;                // groups per launch pair: <= 96 MB
+
+struct GnParams {
+    const uint16_t* x;
+    uint16_t* y;
+    const void* gamma;
+    const void* beta;
+    float* partial;          // [pairs][chunks][2]: chunk mean, sum of squared deviations
+    int64_t group_begin;     // first (sample, group) pair of this launch
+    int64_t group_size;      // Cg * spatial elements, a multiple of 8, < 2^31
+    int32_t spatial;
+    int32_t cg;
+    int32_t groups;
+    int32_t chunks;          // chunks per group
+    float eps;
+};
+
+// Vectors valid in chunk k of a group.
+__device__ __forceinline__ int chunk_vectors(const GnParams& p, int k)
+{
+    const int64_t left = p.group_size - (int64_t)k * kChunk;
+    return (int)((left < kChunk ? left : kChunk) / kVec);
+}
+
+// Load the chunk's vectors; thread vectors past `nv` reload the last valid
+// vector (clamped, so every load is unconditional) and are zeroed.
+template <bool NT>
+__device__ __forceinline__ void load_chunk(const uint16_t* base, int nv, u32x4 (&v)[kVpt])
+{
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        const u32x4 t = load16<NT>(base + (int64_t)(i < nv ? i : nv - 1) * kVec);
+        v[u] = i < nv ? t : u32x4{0, 0, 0, 0};
+    }
+}
+
+// Mean and sum of squared deviations of the chunk held in v (nv valid vectors).
+template <bool X_FP16>
+__device__ __forceinline__ void chunk_moments(const u32x4 (&v)[kVpt], int nv, float* red0,
+                                              float* red1, float& mean, float& m2)
+{
+    float sum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+        float f[8];
+        unpack8<X_FP16>(v[u], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            sum += f[k];
+    }
+    mean = block_sum<kWaves>(sum, red0) / (float)(nv * kVec);
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+        if (u * kBlock + (int)threadIdx.x < nv) {
+            float f[8];
+            unpack8<X_FP16>(v[u], f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float d = f[k] - mean;
+                ss = __builtin_fmaf(d, d, ss);
+            }
+        }
+    }
+    m2 = block_sum<kWaves>(ss, red1);
+}
+
+template <int PARAM>
+__device__ __forceinline__ float param(const void* table, int c)
+{
+    if constexpr (PARAM == QKR_FP32) {
+        return static_cast<const float*>(table)[c];
+    } else {
+        const uint16_t h = static_cast<const uint16_t*>(table)[c];
+        if constexpr (PARAM == QKR_FP16)
+            return (float)__builtin_bit_cast(_Float16, h);
+        else
+            return __uint_as_float((uint32_t)h << 16);
+    }
+}
+
+// Normalise, apply the channel affine and SiLU to the chunk, store it.
+template <bool X_FP16, int PARAM>
+__device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k, int nv,
+                                            const u32x4 (&v)[kVpt], float mean, float rstd)
+{
+    uint16_t* yq = p.y + q * p.group_size + (int64_t)k * kChunk;
+    const int c0 = (int)(q % p.groups) * p.cg;
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        if (i < nv) {
+            const uint32_t e = (uint32_t)(k * kChunk) + (uint32_t)i * kVec;   // < 2^31
+            const int c = c0 + (int)(e / (uint32_t)p.spatial);
+            const float g = param<PARAM>(p.gamma, c);
+            const float b = param<PARAM>(p.beta, c);
+            float f[8], o[8];
+            unpack8<X_FP16>(v[u], f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float t = __builtin_fmaf((f[j] - mean) * rstd, g, b);
+                o[j] = t / (1.0f + __expf(-t));
+            }
+            store16<true>(yq + (int64_t)i * kVec, pack8<X_FP16>(o));
+        }
+    }
+}
+
+// One chunk per group: statistics and output from one read.
+template <bool X_FP16, int PARAM>
+__global__ __launch_bounds__(kBlock) void gn_single_kernel(const GnParams p)
+{
+    __shared__ float red[2][kWaves];
+    const int64_t q = p.group_begin + blockIdx.x;
+    const int nv = chunk_vectors(p, 0);
+    u32x4 v[kVpt];
+    load_chunk<true>(p.x + q * p.group_size, nv, v);
+    float mean, m2;
+    chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
+    const float rstd = __builtin_amdgcn_rsqf(m2 / (float)p.group_size + p.eps);
+    chunk_apply<X_FP16, PARAM>(p, q, 0, nv, v, mean, rstd);
+}
+
+// Several chunks, pass 1: per-chunk mean and sum of squared deviations.
+template <bool X_FP16>
+__global__ __launch_bounds__(kBlock) void gn_stats_kernel(const GnParams p)
+{
+    __shared__ float red[2][kWaves];
+    const int64_t q = p.group_begin + blockIdx.x / p.chunks;
+    const int k = (int)(blockIdx.x % p.chunks);
+    const int nv = chunk_vectors(p, k);
+    u32x4 v[kVpt];
+    load_chunk<false>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
+    float mean, m2;
+    chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
+    if (threadIdx.x == 0) {
+        float* out = p.partial + 2 * (q * p.chunks + k);
+        out[0] = mean;
+        out[1] = m2;
+    }
+}
+
+// Several chunks, pass 2: combine the group's partials, write the chunk.
+template <bool X_FP16, int PARAM>
+__global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
+{
+    __shared__ float red[2][kWaves];
+    const int64_t q = p.group_begin + blockIdx.x / p.chunks;
+    const int k = (int)(blockIdx.x % p.chunks);
+    const int nv = chunk_vectors(p, k);
+    u32x4 v[kVpt];
+    load_chunk<true>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
+
+    const float* part = p.partial + 2 * q * p.chunks;
+    const float last_n = (float)(p.group_size - (int64_t)(p.chunks - 1) * kChunk);
+    float s = 0.0f;
+    for (int i = threadIdx.x; i < p.chunks; i += kBlock) {
+        const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
+        s = __builtin_fmaf(n_i, part[2 * i], s);
+    }
+    const float mean = block_sum<kWaves>(s, red[0]) / (float)p.group_size;
+    float m2 = 0.0f;
+    for (int i = threadIdx.x; i < p.chunks; i += kBlock) {
+        const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
+        const float d = part[2 * i] - mean;
+        m2 += __builtin_fmaf(n_i * d, d, part[2 * i + 1]);
+    }
+    const float rstd = __builtin_amdgcn_rsqf(block_sum<kWaves>(m2, red[1]) / (float)p.group_size
+                                             + p.eps);
+    chunk_apply<X_FP16, PARAM>(p, q, k, nv, v, mean, rstd);
+}
+
+using GnFn = void (*)(GnParams);
+
+template <bool XF>
+GnFn pick_single(int prm)
+{
+    return prm == QKR_FP32 ? gn_single_kernel<XF, QKR_FP32>
+         : prm == QKR_FP16 ? gn_single_kernel<XF, QKR_FP16> : gn_single_kernel<XF, QKR_BF16>;
+}
+
+template <bool XF>
+GnFn pick_apply(int prm)
+{
+    return prm == QKR_FP32 ? gn_apply_kernel<XF, QKR_FP32>
+         : prm == QKR_FP16 ? gn_apply_kernel<XF, QKR_FP16> : gn_apply_kernel<XF, QKR_BF16>;
+}
+
+int launch(GnFn fn, int64_t blocks, const GnParams& p, hipStream_t stream)
+{
+    GnParams copy = p;
+    void* args[] = {&copy};
+    if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)blocks), dim3(kBlock),
+                        args, 0, stream) != hipSuccess)
+        return QKR_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? QKR_OK : QKR_ERR_HIP;
+}
+
+// Shape checks shared by the size query and the call; sets chunks and pairs.
+int check_shape(int64_t n, int32_t channels, int64_t spatial, int32_t groups, int64_t* chunks,
+                int64_t* pairs)
+{
+    if (n < 0 || channels < 1 || groups < 1 || channels % groups)
+        return QKR_ERR_SHAPE;
+    if (spatial < kVec || spatial % kVec || spatial >= (1ll << 31))
+        return QKR_ERR_UNSUPPORTED;
+    const int64_t gsize = (int64_t)(channels / groups) * spatial;
+    if (gsize >= (1ll << 31))
+        return QKR_ERR_SHAPE;
+    *chunks = (gsize + kChunk - 1) / kChunk;
+    if (n > ((1ll << 31) - 1) / groups)
+        return QKR_ERR_SHAPE;
+    *pairs = n * groups;
+    if (*pairs * *chunks >= (1ll << 31))
+        return QKR_ERR_SHAPE;
+    return QKR_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channels, int64_t spatial,
+                                                      int32_t groups)
+{
+    int64_t chunks = 0, pairs = 0;
+    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs);
+    if (rc != QKR_OK)
+        return rc;
+    return chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
+}
+
+extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels,
+                                   int64_t spatial, int32_t groups, const void* gamma,
+                                   const void* beta, int32_t param_dtype, float eps, int32_t dtype,
+                                   void* workspace, int64_t workspace_bytes, void* stream)
+{
+    if (dtype < QKR_BF16 || dtype > QKR_FP32 || param_dtype < QKR_BF16 || param_dtype > QKR_FP32)
+        return QKR_ERR_ARG;
+    if (dtype == QKR_FP32)
+        return QKR_ERR_UNSUPPORTED;
+    if (!(eps > 0.0f) || !isfinite(eps))
+        return QKR_ERR_ARG;
+    int64_t chunks = 0, pairs = 0;
+    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs);
+    if (rc != QKR_OK)
+        return rc;
+    if (n == 0)
+        return QKR_OK;
+    if (!x || !y || !gamma || !beta)
+        return QKR_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta))
+        return QKR_ERR_ALIGN;
+    const int64_t gsize = (int64_t)(channels / groups) * spatial;
+    const uintptr_t bytes = (uintptr_t)(pairs * gsize) * 2u;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+    if (xa != ya && xa < ya + bytes && ya < xa + bytes)
+        return QKR_ERR_ARG;
+    const int64_t need = chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return QKR_ERR_WORKSPACE;
+
+    GnParams p;
+    p.x = static_cast<const uint16_t*>(x);
+    p.y = static_cast<uint16_t*>(y);
+    p.gamma = gamma;
+    p.beta = beta;
+    p.partial = static_cast<float*>(workspace);
+    p.group_begin = 0;
+    p.group_size = gsize;
+    p.spatial = (int32_t)spatial;
+    p.cg = channels / groups;
+    p.groups = groups;
+    p.chunks = (int32_t)chunks;
+    p.eps = eps;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool xf = dtype == QKR_FP16;
+
+    if (chunks == 1)
+        return launch(xf ? pick_single<true>(param_dtype) : pick_single<false>(param_dtype), pairs,
+                      p, s);
+
+    GnFn stats = xf ? gn_stats_kernel<true> : gn_stats_kernel<false>;
+    GnFn apply = xf ? pick_apply<true>(param_dtype) : pick_apply<false>(param_dtype);
+    int64_t slab = kSlabBytes / (gsize * 2);
+    if (slab < 1)
+        slab = 1;
+    for (int64_t g0 = 0; g0 < pairs; g0 += slab) {
+        const int64_t m = pairs - g0 < slab ? pairs - g0 : slab;
+        p.group_begin = g0;
+        int r = launch(stats, m * chunks, p, s);
+        if (r == QKR_OK)
+            r = launch(apply, m * chunks, p, s);
+        if (r != QKR_OK)
+            return r;
+    }
+    return QKR_OK;
+}

@@ -507,10 +507,11 @@ extern "C" const char* qknorm_rope_strerror(int status)
     case QKR_ERR_NULL: return "a required pointer is NULL";
     case QKR_ERR_SHAPE: return "tokens or heads out of range";
     case QKR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case QKR_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case QKR_ERR_UNSUPPORTED: return "unsupported size or dtype (head_dim 64/128; hidden or spatial a multiple of 8)";
     case QKR_ERR_MODE: return "pass either qkv, or q and/or k (not both, not neither)";
     case QKR_ERR_HIP: return "HIP launch or query failed";
     case QKR_ERR_ARG: return "eps must be finite and > 0; enum argument out of range";
+    case QKR_ERR_WORKSPACE: return "workspace missing or smaller than required";
     default: return "unknown status";
     }
 }

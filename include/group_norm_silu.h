@@ -1,0 +1,76 @@
+/*
+ * group_norm_silu.h -- C ABI of the fused group norm + SiLU step (VAE) for AMD
+ * Instinct MI355X (gfx950), built into the same library as qknorm_rope.h
+ * (libqknorm_rope.so).
+ *
+ * The operation is the "group_norm_silu" (VAE) follow-up that
+ * TensorRT-Model-Connect PR "perf(diffusion): fused qknorm rope Flux 2.0"
+ * names (section "Not in this PR - follow-ups").  The page gives only the
+ * name; this library implements the plain definition, a group normalisation
+ * with a per-channel affine followed by SiLU:
+ *
+ *   x, y [n, channels, spatial] contiguous (spatial = H*W, or T*H*W);
+ *   G = groups, Cg = channels / G; for sample i and group g, over the
+ *   Cg * spatial elements of channels g*Cg .. g*Cg + Cg - 1:
+ *     mean = average;  var = average squared deviation (biased)
+ *     t    = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c]
+ *     y    = t / (1 + exp(-t))
+ *
+ * Math is fp32; y is rounded once, to nearest even, to x's dtype.  Large
+ * groups are reduced in chunks whose partial statistics (mean and sum of
+ * squared deviations per chunk) go to a caller-owned workspace; the chunks
+ * are then combined exactly as a two-level reduction (Chan et al.).
+ *
+ * Pointers are DEVICE pointers owned by the caller; the library allocates,
+ * frees and synchronises nothing.  y may be x itself or a buffer that does
+ * not overlap it.  Calls that share a workspace must not run concurrently.
+ */
+#ifndef GROUP_NORM_SILU_H
+#define GROUP_NORM_SILU_H
+
+#include <stdint.h>
+
+#include "qknorm_rope.h" /* status codes and dtype constants */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * dit_group_norm_silu_workspace_size -- bytes of workspace a call with these
+ * sizes needs (0 when every group fits one chunk), or a negative QKR_ERR_*
+ * code for sizes dit_group_norm_silu would reject.
+ */
+int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channels, int64_t spatial,
+                                           int32_t groups);
+
+/*
+ * dit_group_norm_silu -- group norm + SiLU of an [n, channels, spatial] tensor.
+ *
+ * n                >= 0 (0 is a no-op returning QKR_OK once scalars are valid).
+ * channels, groups >= 1, groups divides channels.
+ * spatial          >= 8, a multiple of 8; channels/groups * spatial < 2^31.
+ * gamma, beta      [channels] of param_dtype (QKR_BF16, QKR_FP16, QKR_FP32).
+ * eps              finite and > 0, added to the variance inside the root.
+ * dtype            QKR_BF16 or QKR_FP16 (x and y).
+ * workspace        device buffer of at least
+ *                  dit_group_norm_silu_workspace_size(...) bytes (may be NULL
+ *                  when that size is 0), 16-byte aligned; its contents on
+ *                  entry do not matter and are left undefined.
+ * stream           a hipStream_t (NULL = the default stream).
+ *
+ * x, y, gamma and beta must be 16-byte aligned.  Returns QKR_OK or a negative
+ * QKR_ERR_* code (QKR_ERR_WORKSPACE for a missing or short workspace,
+ * QKR_ERR_ARG also when y partly overlaps x); all checks happen before any HIP
+ * call and nothing is enqueued on error.
+ */
+int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int64_t spatial,
+                        int32_t groups, const void* gamma, const void* beta, int32_t param_dtype,
+                        float eps, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROUP_NORM_SILU_H */

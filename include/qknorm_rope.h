@@ -44,7 +44,8 @@ enum {
     QKR_ERR_UNSUPPORTED = -4, /* head_dim not 64/128, or an unsupported dtype        */
     QKR_ERR_MODE = -5,        /* not exactly one of {qkv} / {q and/or k}             */
     QKR_ERR_HIP = -6,         /* the kernel launch (or an attribute query) failed     */
-    QKR_ERR_ARG = -7          /* eps not finite and > 0, or an enum out of range      */
+    QKR_ERR_ARG = -7,         /* eps not finite and > 0, or an enum out of range      */
+    QKR_ERR_WORKSPACE = -8    /* workspace missing or smaller than required           */
 };
 
 /* Element types. */

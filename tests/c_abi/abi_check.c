@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "fuse_scale_shift.h"
+#include "group_norm_silu.h"
 #include "qknorm_rope.h"
 
 #define EXPECT(call, code)                                                          \
@@ -23,6 +24,7 @@ int main(void)
 {
     void* a = (void*)(uintptr_t)0x10000;      /* aligned fake device addresses */
     void* b = (void*)(uintptr_t)0x90000;
+    void* far = (void*)(uintptr_t)0x40000000;  /* beyond any x range used below */
     void* mis = (void*)(uintptr_t)0x10004;
     const float* g = (const float*)a;
 
@@ -60,6 +62,18 @@ int main(void)
            QKR_ERR_SHAPE);
     EXPECT(dit_fuse_scale_shift(a, b, 4, 6144, 1, NULL, a, QKR_FP32, 1e-6f, QKR_BF16, NULL),
            QKR_ERR_NULL);
+    if (dit_group_norm_silu_workspace_size(1, 512, 128 * 128, 32) != 32 * 16 * 8) {
+        printf("FAIL workspace size\n");
+        return 1;
+    }
+    EXPECT(dit_group_norm_silu(a, b, 1, 512, 128 * 128, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16, NULL,
+                               0, NULL), QKR_ERR_ARG);          /* y inside x's 16 MB */
+    EXPECT(dit_group_norm_silu(a, far, 1, 512, 128 * 128, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16,
+                               NULL, 0, NULL), QKR_ERR_WORKSPACE);
+    EXPECT(dit_group_norm_silu(a, b, 1, 512, 100, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16, NULL, 0,
+                               NULL), QKR_ERR_UNSUPPORTED);
+    EXPECT(dit_group_norm_silu(a, b, 0, 512, 64, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16, NULL, 0,
+                               NULL), QKR_OK);
     printf("ok\n");
     return 0;
 }

@@ -25,7 +25,8 @@ def declared_functions():
         if h.endswith(".h"):
             with open(os.path.join(INCLUDE, h)) as f:
                 text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-            names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M))
+            names |= set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text,
+                                    flags=re.M))
     return names
 
 
@@ -166,3 +167,51 @@ def test_fuse_scale_shift_binding_checks_shapes():
         qkr.fuse_scale_shift(x, s[:, :32], s[:, :32])
     with pytest.raises(ValueError):      # CPU tensors are refused
         qkr.fuse_scale_shift(x, s[:2], s[:2])
+
+
+# ----------------------------------------------------------------------------- group norm + SiLU
+
+
+def gn(**over):
+    args = dict(x=A, y=A + 0x1000000, n=2, channels=64, spatial=4096, groups=32, gamma=A, beta=A,
+                param_dtype=b.QKR_FP32, eps=1e-6, dtype=b.QKR_BF16, workspace=0, workspace_bytes=0,
+                stream=0)
+    args.update(over)
+    return qkr.dit_group_norm_silu_raw(**args)
+
+
+def test_group_norm_workspace_size():
+    ws = qkr.group_norm_silu_workspace_size
+    assert ws(1, 512, 128 * 128, 32) == 32 * 16 * 8          # 16 chunks of 16384 per group
+    assert ws(1, 128, 1024 * 1024, 32) == 32 * 256 * 8
+    assert ws(2, 64, 4096, 32) == 0                         # 8192-element groups: one chunk
+    assert ws(1, 6, 16384 * 2 + 8, 2) == 2 * 7 * 8          # 3*(32776) -> 7 chunks
+    assert ws(1, 64, 12, 32) == b.QKR_ERR_UNSUPPORTED       # spatial not a multiple of 8
+    assert ws(1, 60, 64, 32) == b.QKR_ERR_SHAPE             # groups do not divide channels
+    assert ws(-1, 64, 64, 32) == b.QKR_ERR_SHAPE
+    assert ws(1, 2, 1 << 31, 1) == b.QKR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=b.QKR_FP32), b.QKR_ERR_UNSUPPORTED),
+    (dict(dtype=5), b.QKR_ERR_ARG),
+    (dict(param_dtype=-1), b.QKR_ERR_ARG),
+    (dict(eps=0.0), b.QKR_ERR_ARG),
+    (dict(groups=7), b.QKR_ERR_SHAPE),
+    (dict(channels=0), b.QKR_ERR_SHAPE),
+    (dict(spatial=100), b.QKR_ERR_UNSUPPORTED),
+    (dict(n=-3), b.QKR_ERR_SHAPE),
+    (dict(x=0), b.QKR_ERR_NULL),
+    (dict(gamma=0), b.QKR_ERR_NULL),
+    (dict(beta=MIS), b.QKR_ERR_ALIGN),
+    (dict(y=A + 4096), b.QKR_ERR_ARG),                         # partial overlap
+    (dict(spatial=65536), b.QKR_ERR_WORKSPACE),                # needs a workspace
+    (dict(spatial=65536, workspace=A + 0x9000000, workspace_bytes=8), b.QKR_ERR_WORKSPACE),
+    (dict(spatial=65536, workspace=MIS, workspace_bytes=1 << 20), b.QKR_ERR_WORKSPACE),
+])
+def test_group_norm_rejects_before_any_hip_call(over, code):
+    assert gn(**over) == code
+
+
+def test_group_norm_zero_samples_is_a_no_op():
+    assert gn(n=0, x=0, y=0, gamma=0, beta=0) == b.QKR_OK
