@@ -10,8 +10,8 @@
 //     one at a time: thread j holds vectors j, j+256, ... of the row (8
 //     elements each, 16-byte non-temporal loads), VPT vectors per thread, so
 //     each load instruction of the workgroup reads one contiguous 4 KB and the
-//     whole row sits in registers; the next row's loads are issued before the
-//     current row's arithmetic;
+//     whole row sits in registers; the loads of the next two rows are in
+//     flight while the current row is reduced;
 //   * the modulation vectors (scale and shift, the same channels as the
 //     thread's row vectors) stay in registers across the run and are reloaded
 //     only when the batch changes, so they cost L2 traffic once per run, not
@@ -102,7 +102,8 @@ __device__ __forceinline__ void load_mods(const FssParams& p, int64_t mrow, int 
     }
 }
 
-template <int VPT, bool X_FP16, int MOD>
+// AHEAD: rows whose loads are in flight beyond the one being reduced (1 or 2).
+template <int VPT, bool X_FP16, int MOD, int AHEAD>
 __global__ __launch_bounds__(kBlock) void fuse_scale_shift_kernel(const FssParams p)
 {
     constexpr int NV = mod_vecs<MOD>();
@@ -113,14 +114,20 @@ __global__ __launch_bounds__(kBlock) void fuse_scale_shift_kernel(const FssParam
     const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
     const int64_t r1 = r0 + p.rows_per_block < p.rows ? r0 + p.rows_per_block : p.rows;
 
-    u32x4 v[VPT], vn[VPT], sc[VPT * NV], sh[VPT * NV];
+    u32x4 v[VPT], vn[VPT], vnn[VPT], sc[VPT * NV], sh[VPT * NV];
     load_row<VPT>(p.x + r0 * C, nvec, v);
+    if (AHEAD > 1 && r0 + 1 < r1)
+        load_row<VPT>(p.x + (r0 + 1) * C, nvec, vn);
     int64_t batch = r0 / p.rows_per_batch;
     load_mods<VPT, MOD, NV>(p, batch * C, nvec, sc, sh);
 
     for (int64_t r = r0; r < r1; ++r) {
-        if (r + 1 < r1)
+        if (AHEAD > 1) {
+            if (r + 2 < r1)
+                load_row<VPT>(p.x + (r + 2) * C, nvec, vnn);
+        } else if (r + 1 < r1) {
             load_row<VPT>(p.x + (r + 1) * C, nvec, vn);
+        }
 #pragma unroll
         for (int u = 0; u < VPT; ++u)
             if (u * kBlock + tid >= nvec)
@@ -178,21 +185,26 @@ __global__ __launch_bounds__(kBlock) void fuse_scale_shift_kernel(const FssParam
             }
         }
 #pragma unroll
-        for (int u = 0; u < VPT; ++u)
+        for (int u = 0; u < VPT; ++u) {
             v[u] = vn[u];
+            if (AHEAD > 1)
+                vn[u] = vnn[u];
+        }
     }
 }
 
 using FssFn = void (*)(FssParams);
 
+constexpr int kRowsAhead = 2;
+
 template <int VPT, bool XF>
 FssFn select_mod(int mod)
 {
     if (mod == QKR_FP32)
-        return fuse_scale_shift_kernel<VPT, XF, QKR_FP32>;
+        return fuse_scale_shift_kernel<VPT, XF, QKR_FP32, kRowsAhead>;
     if (mod == QKR_FP16)
-        return fuse_scale_shift_kernel<VPT, XF, QKR_FP16>;
-    return fuse_scale_shift_kernel<VPT, XF, QKR_BF16>;
+        return fuse_scale_shift_kernel<VPT, XF, QKR_FP16, kRowsAhead>;
+    return fuse_scale_shift_kernel<VPT, XF, QKR_BF16, kRowsAhead>;
 }
 
 template <int VPT>
@@ -211,11 +223,12 @@ FssFn select_kernel(int vpt, bool xf, int mod)
     }
 }
 
-// Rows per workgroup: runs of 4 rows amortise the modulation loads 4x and
-// still leave about 8000 workgroups on a 32K-row call; shorter runs for
-// small calls keep the grid large enough to fill the chip (measured over
-// 1..32 rows per workgroup on 32760 x 5120 and 4608 x 6144).
-int64_t rows_per_block(int64_t rows) { return rows >= 16384 ? 4 : rows >= 4096 ? 2 : 1; }
+// Rows per workgroup: runs of 3 rows (loads two rows ahead) amortise the
+// modulation loads and still leave about 11000 workgroups on a 32K-row call;
+// shorter runs for small calls keep the grid large enough to fill the chip
+// (measured over 1..32 rows per workgroup and 1..2 rows ahead on 32760 x 5120
+// and 4608 x 6144).
+int64_t rows_per_block(int64_t rows) { return rows >= 16384 ? 3 : rows >= 4096 ? 2 : 1; }
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 

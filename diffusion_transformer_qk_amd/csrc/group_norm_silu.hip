@@ -137,7 +137,7 @@ __device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k,
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float t = __builtin_fmaf((f[j] - mean) * rstd, g, b);
-                o[j] = t / (1.0f + __expf(-t));
+                o[j] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
             }
             store16<true>(yq + (int64_t)i * kVec, pack8<X_FP16>(o));
         }
