@@ -11,14 +11,14 @@
 //     squared deviations) in the workspace, then gn_apply_kernel combines
 //     the group's partials with the pairwise update (sum n_i m_i / N, then
 //     sum M2_i + n_i (m_i - m)^2) in a fixed order, so every workgroup of a
-//     group gets the same statistics, and writes y for its chunk.  The host
-//     runs the two kernels over slabs of groups small enough for the slab to
-//     stay in the 256 MB Infinity Cache between them: the stats pass reads
-//     with ordinary loads, the apply pass re-reads with non-temporal loads
-//     and writes non-temporally.
+//     group gets the same statistics, re-reads its chunk and writes y.  The
+//     host runs the two kernels over slabs of groups of at most kSlabBytes
+//     (the sweep's best; the second read is mostly served from HBM, not the
+//     Infinity Cache): the stats pass reads with ordinary loads, the apply
+//     pass re-reads with non-temporal loads and writes non-temporally.
 // Per vector of 8 elements (spatial is a multiple of 8, so a vector never
 // straddles channels): t = fma((x - mean) * rstd, gamma[c], beta[c]),
-// y = t / (1 + exp(-t)), packed with round-to-nearest-even.
+// y = t * rcp(1 + exp(-t)), packed with round-to-nearest-even.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -72,9 +72,19 @@ __device__ __forceinline__ void load_chunk(const uint16_t* base, int nv, u32x4 (
     }
 }
 
+// Make the compiler forget what v holds, so the fp32 values unpacked from it
+// are not kept alive (64 registers) from one pass over the chunk to the next
+// but unpacked again from the 32 packed registers.
+__device__ __forceinline__ void forget_unpacked(u32x4 (&v)[kVpt])
+{
+#pragma unroll
+    for (int u = 0; u < kVpt; ++u)
+        __asm__ volatile("" : "+v"(v[u]));
+}
+
 // Mean and sum of squared deviations of the chunk held in v (nv valid vectors).
 template <bool X_FP16>
-__device__ __forceinline__ void chunk_moments(const u32x4 (&v)[kVpt], int nv, float* red0,
+__device__ __forceinline__ void chunk_moments(u32x4 (&v)[kVpt], int nv, float* red0,
                                               float* red1, float& mean, float& m2)
 {
     float sum = 0.0f;
@@ -87,6 +97,7 @@ __device__ __forceinline__ void chunk_moments(const u32x4 (&v)[kVpt], int nv, fl
             sum += f[k];
     }
     mean = block_sum<kWaves>(sum, red0) / (float)(nv * kVec);
+    forget_unpacked(v);
     float ss = 0.0f;
 #pragma unroll
     for (int u = 0; u < kVpt; ++u) {
@@ -101,6 +112,7 @@ __device__ __forceinline__ void chunk_moments(const u32x4 (&v)[kVpt], int nv, fl
         }
     }
     m2 = block_sum<kWaves>(ss, red1);
+    forget_unpacked(v);
 }
 
 template <int PARAM>

@@ -193,3 +193,24 @@ def test_partial_overlap_and_misalignment_are_rejected():
     with pytest.raises(qkr.QkrError) as e:
         qkr.fuse_scale_shift(xm, s, s)
     assert e.value.status == qkr.binding.QKR_ERR_ALIGN
+
+
+def test_byte_offsets_beyond_4gib_in_place():
+    """[420000, 5120] bf16 = 4.3 GB in place: rows on both sides of the 2^32-byte
+    offset (row 419430 straddles it) against the oracle.  The rows repeat a
+    1024-row block; one modulation row."""
+    rows, hidden, B = 420000, 5120, 1024
+    block, sc, sh = wl.adaln_inputs(4343, B, hidden, 1, "bf16", "fp32")
+    blk = block.to(DEV)
+    x = torch.empty((rows, hidden), dtype=torch.bfloat16, device=DEV)
+    for i in range(0, rows, B):
+        x[i:i + B].copy_(blk[:min(B, rows - i)])
+    qkr.fuse_scale_shift(x, sc.to(DEV), sh.to(DEV), out=x, rows_per_batch=rows)
+    torch.cuda.synchronize()
+    samples = [0, 1, 1023, 1024, 209715, 419429, 419430, 419431, rows - 1]
+    idx = torch.tensor(samples)
+    xs = block[idx % B]
+    y, n = oracle_rows(xs, "bf16", sc, sh, len(samples), wl.EPS)
+    m = check_rows(_decode(x[idx.to(DEV)], "bf16"), y, n, sc, sh, len(samples), 0, "bf16",
+                   ">4GiB rows")
+    print("beyond 4 GiB max_abs", m)

@@ -198,3 +198,67 @@ def test_zero_samples_is_a_no_op():
     out = qkr.group_norm_silu(x, p, p, 4)
     torch.cuda.synchronize()
     assert out.shape == x.shape
+
+
+def test_repeated_calls_reuse_one_workspace():
+    """Back-to-back calls on one workspace, then in place: identical bits."""
+    n, channels, spatial, groups = 2, 64, 64 * 64, 8            # 8 groups of 2 chunks
+    x, g, b = wl.gn_inputs(31, n, channels, spatial, "bf16", "fp32")
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    ws = torch.empty(qkr.group_norm_silu_workspace_size(n, channels, spatial, groups),
+                     dtype=torch.uint8, device=DEV)
+    outs = [qkr.group_norm_silu(xd, gd, bd, groups, workspace=ws) for _ in range(4)]
+    qkr.group_norm_silu(xd, gd, bd, groups, out=xd, workspace=ws)
+    torch.cuda.synchronize()
+    for o in outs[1:] + [xd]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    ref = oracle_groups(x, "bf16", channels, spatial, groups, g, b, wl.EPS)
+    check_groups(_decode(outs[0], "bf16"), ref, channels // groups * spatial, "bf16", "repeat")
+
+
+def test_graph_capture_replays_match_eager():
+    """The two-pass kernels recorded into a graph: every replay, with eager
+    work and synchronisation between replays, equals the eager result."""
+    n, channels, spatial, groups = 1, 64, 128 * 128, 8             # 8 chunks per group
+    x, g, b = wl.gn_inputs(77, n, channels, spatial, "bf16", "fp32")
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    eager = qkr.group_norm_silu(xd, gd, bd, groups)
+    ws = torch.empty(qkr.group_norm_silu_workspace_size(n, channels, spatial, groups),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(xd)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            qkr.group_norm_silu(xd, gd, bd, groups, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        ws.fill_(0x7F)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+def test_byte_offsets_beyond_4gib_in_place():
+    """[260, 128, 256, 256] bf16 = 4.4 GB in place, 32 groups of 16 chunks:
+    8320 groups in 44 slabs; groups on both sides of the 2^32-byte offset
+    (group 8192 starts there) against the oracle.  The samples repeat a
+    4-sample block."""
+    n, channels, spatial, groups, B = 260, 128, 256 * 256, 32, 4
+    block, g, b = wl.gn_inputs(4444, B, channels, spatial, "bf16", "fp32")
+    blk = block.to(DEV)
+    x = torch.empty((n, channels, spatial), dtype=torch.bfloat16, device=DEV)
+    for i in range(0, n, B):
+        x[i:i + B].copy_(blk[:min(B, n - i)])
+    qkr.group_norm_silu(x, g.to(DEV), b.to(DEV), groups, out=x)
+    torch.cuda.synchronize()
+    gsize = channels // groups * spatial
+    flat = x.view(-1)
+    for q in (0, 8191, 8192, 8193, n * groups - 1):
+        ref = oracle_groups(block, "bf16", channels, spatial, groups, g, b, wl.EPS,
+                            q % (B * groups), q % (B * groups) + 1)
+        got = _decode(flat[q * gsize:(q + 1) * gsize], "bf16")
+        check_groups(got, ref, gsize, "bf16", ">4GiB group %d" % q)

@@ -273,6 +273,39 @@ def test_large_workload_sampled_and_layout_parity(style):
     print("large", style, "sampled max_abs", m)
 
 
+def test_byte_offsets_beyond_4gib():
+    """[140000, 3*40*128] bf16 = 4.3 GB, in the headline's launch configuration:
+    tokens on both sides of the 2^32-byte offset (token 139810 straddles it)
+    against the oracle, and V untouched everywhere.  The activations repeat a
+    2048-token block (the pass is per token, so each sampled token is a full
+    case); cos/sin come from a 28 x 50 x 100 position grid."""
+    T, H, D, B = 140000, 40, 128, 2048
+    block = wl.fused_qkv(4242, B, H, D, "bf16")
+    qg, kg = wl.norm_weights(4242, D)
+    cos, sin = wl.rope_tables(wl.grid_positions((28, 50, 100)), (22, 21, 21), D, "interleaved")
+    blk = block.to(DEV)
+    x = torch.empty((T, 3 * H * D), dtype=torch.bfloat16, device=DEV)
+    for i in range(0, T, B):
+        x[i:i + B].copy_(blk[:min(B, T - i)])
+    qkr.qknorm_rope_fused(x, q_gamma=dev(qg), k_gamma=dev(kg), cos=dev(cos), sin=dev(sin),
+                          style="interleaved")
+    torch.cuda.synchronize()
+    info = qkr.kernel_info(D, "shared", qkr.binding.QKR_FP32, "interleaved",
+                           qkr.binding.QKR_BF16, heads=H, tokens=T)
+    assert info["die_runs"] == 1 and info["heads_in_flight"] == 10
+    for i in range(0, T, B):
+        n = min(B, T - i)
+        assert torch.equal(x[i:i + n, 2 * H * D:], blk[:n, 2 * H * D:]), "V changed"
+    samples = [0, 1, B - 1, B, 69905, 139809, 139810, 139811, T - 2, T - 1]
+    idx = torch.tensor(samples)
+    rows = block[idx % B]
+    q_ref, k_ref = oracle_fused(rows, "bf16", H, D, qg, kg, cos[idx], sin[idx], "interleaved")
+    got = _decode(x[idx.to(DEV)], "bf16").reshape(len(samples), 3, H, D)
+    m = max(check_close(got[:, 0], q_ref, "bf16", ">4GiB Q"),
+            check_close(got[:, 1], k_ref, "bf16", ">4GiB K"))
+    print("beyond 4 GiB max_abs", m)
+
+
 @pytest.mark.parametrize("heads,head_dim", [(3, 128), (24, 128), (48, 128), (72, 64), (100, 64)])
 def test_die_order_every_unroll(heads, head_dim):
     """8200 tokens = 4100 workgroups: the per-die token runs (with a ragged

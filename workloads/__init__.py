@@ -84,13 +84,19 @@ def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
-def positions(w: Workload) -> np.ndarray:
-    """Integer positions [tokens, n_axes], row-major over ``w.grid``."""
-    axes = [np.arange(n, dtype=np.int64) for n in w.grid]
+def grid_positions(grid: tuple, text_tokens: int = 0) -> np.ndarray:
+    """Integer positions [text_tokens + prod(grid), len(grid)]: text tokens at
+    the origin, then the grid row-major."""
+    axes = [np.arange(n, dtype=np.int64) for n in grid]
     mesh = np.meshgrid(*axes, indexing="ij")
     grid_pos = np.stack([m.reshape(-1) for m in mesh], axis=1)
-    text = np.zeros((w.text_tokens, len(w.grid)), dtype=np.int64)
-    pos = np.concatenate([text, grid_pos], axis=0)
+    text = np.zeros((text_tokens, len(grid)), dtype=np.int64)
+    return np.concatenate([text, grid_pos], axis=0)
+
+
+def positions(w: Workload) -> np.ndarray:
+    """Integer positions [tokens, n_axes], row-major over ``w.grid``."""
+    pos = grid_positions(w.grid, w.text_tokens)
     assert pos.shape[0] == w.tokens, (pos.shape, w.tokens)
     return pos
 
