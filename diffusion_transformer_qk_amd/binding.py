@@ -10,6 +10,7 @@ loudly.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -140,6 +141,26 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
+def _call_context(ref, tensors, stream):
+    """(device context, raw hipStream_t) for a call on ``ref``'s device.
+
+    Every tensor given must live on that device; the call runs with it as the
+    current device, so a NULL (default) stream means that device's.
+    """
+    torch = _torch()
+    for t in tensors:
+        if t is not None and t.device != ref.device:
+            raise ValueError("all tensors must be on one device (%s)" % ref.device)
+    if stream is None:
+        raw = torch.cuda.current_stream(ref.device).cuda_stream if ref.is_cuda else 0
+    elif isinstance(stream, int):
+        raw = stream
+    else:
+        raw = stream.cuda_stream
+    ctx = torch.cuda.device(ref.device) if ref.is_cuda else contextlib.nullcontext()
+    return ctx, raw
+
+
 def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
                       cos=None, sin=None, eps: float = 1e-6, heads: int | None = None,
                       head_dim: int | None = None, cos_layout: str = "shared",
@@ -189,16 +210,12 @@ def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
     for g in (q_gamma, k_gamma):
         if g is not None and (g.dtype != torch.float32 or g.numel() != head_dim):
             raise ValueError("gamma must be float32 [head_dim]")
-    if stream is None:
-        stream_ptr = torch.cuda.current_stream(ref.device).cuda_stream if ref.is_cuda else 0
-    elif isinstance(stream, int):
-        stream_ptr = stream
-    else:
-        stream_ptr = stream.cuda_stream
-    status = qknorm_rope_fused_raw(
-        _ptr(qkv), _ptr(q), _ptr(k), tokens, heads, head_dim, _ptr(q_gamma), _ptr(k_gamma),
-        float(eps), _ptr(cos), _ptr(sin), LAYOUTS[cos_layout], _table_code(cos),
-        STYLES[style], _x_code(ref), stream_ptr)
+    ctx, stream_ptr = _call_context(ref, (qkv, q, k, q_gamma, k_gamma, cos, sin), stream)
+    with ctx:
+        status = qknorm_rope_fused_raw(
+            _ptr(qkv), _ptr(q), _ptr(k), tokens, heads, head_dim, _ptr(q_gamma), _ptr(k_gamma),
+            float(eps), _ptr(cos), _ptr(sin), LAYOUTS[cos_layout], _table_code(cos),
+            STYLES[style], _x_code(ref), stream_ptr)
     _check(status)
 
 
@@ -259,15 +276,12 @@ def fuse_scale_shift(x, scale, shift, *, out=None, eps: float = 1e-6,
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("out must match x in shape and dtype")
-    if stream is None:
-        stream_ptr = torch.cuda.current_stream(x.device).cuda_stream if x.is_cuda else 0
-    elif isinstance(stream, int):
-        stream_ptr = stream
-    else:
-        stream_ptr = stream.cuda_stream
-    _check(dit_fuse_scale_shift_raw(_ptr(x), _ptr(out), rows, hidden, rows_per_batch,
-                                    _ptr(scale), _ptr(shift), _mod_code(scale), float(eps),
-                                    _x_code(x), stream_ptr))
+    ctx, stream_ptr = _call_context(x, (out, scale, shift), stream)
+    with ctx:
+        status = dit_fuse_scale_shift_raw(_ptr(x), _ptr(out), rows, hidden, rows_per_batch,
+                                          _ptr(scale), _ptr(shift), _mod_code(scale), float(eps),
+                                          _x_code(x), stream_ptr)
+    _check(status)
     return out
 
 
@@ -316,13 +330,10 @@ def group_norm_silu(x, gamma, beta, groups: int, *, out=None, eps: float = 1e-6,
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("out must match x in shape and dtype")
-    if stream is None:
-        stream_ptr = torch.cuda.current_stream(x.device).cuda_stream if x.is_cuda else 0
-    elif isinstance(stream, int):
-        stream_ptr = stream
-    else:
-        stream_ptr = stream.cuda_stream
-    _check(dit_group_norm_silu_raw(_ptr(x), _ptr(out), n, channels, spatial, groups, _ptr(gamma),
-                                   _ptr(beta), _mod_code(gamma), float(eps), _x_code(x),
-                                   _ptr(workspace), ws_bytes, stream_ptr))
+    ctx, stream_ptr = _call_context(x, (out, gamma, beta, workspace), stream)
+    with ctx:
+        status = dit_group_norm_silu_raw(_ptr(x), _ptr(out), n, channels, spatial, groups,
+                                         _ptr(gamma), _ptr(beta), _mod_code(gamma), float(eps),
+                                         _x_code(x), _ptr(workspace), ws_bytes, stream_ptr)
+    _check(status)
     return out

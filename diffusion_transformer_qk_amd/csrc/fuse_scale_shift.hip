@@ -29,11 +29,14 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "host_common.h"
 #include "fuse_scale_shift.h"
 
 namespace {
 
 using namespace qkr_dev;
+using qkr_host::aligned16;
+using qkr_host::overlaps;
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;   // one row per workgroup
@@ -230,7 +233,6 @@ FssFn select_kernel(int vpt, bool xf, int mod)
 // and 4608 x 6144).
 int64_t rows_per_block(int64_t rows) { return rows >= 16384 ? 3 : rows >= 4096 ? 2 : 1; }
 
-bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 }  // namespace
 
@@ -254,9 +256,12 @@ extern "C" int dit_fuse_scale_shift(const void* x, void* y, int64_t rows, int32_
         return QKR_ERR_NULL;
     if (!aligned16(x) || !aligned16(y) || !aligned16(scale) || !aligned16(shift))
         return QKR_ERR_ALIGN;
-    const uintptr_t bytes = (uintptr_t)rows * (uintptr_t)hidden * 2u;
-    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
-    if (xa != ya && xa < ya + bytes && ya < xa + bytes)
+    // y is x itself or disjoint from it, and never overlaps the modulation
+    const uint64_t bytes = (uint64_t)rows * (uint64_t)hidden * 2u;
+    const uint64_t mod_bytes = (uint64_t)((rows + rows_per_batch - 1) / rows_per_batch) *
+                               (uint64_t)hidden * (mod_dtype == QKR_FP32 ? 4u : 2u);
+    if ((x != y && overlaps(x, bytes, y, bytes)) || overlaps(y, bytes, scale, mod_bytes) ||
+        overlaps(y, bytes, shift, mod_bytes))
         return QKR_ERR_ARG;
 
     FssParams p;
@@ -274,7 +279,5 @@ extern "C" int dit_fuse_scale_shift(const void* x, void* y, int64_t rows, int32_
     const int64_t blocks = (rows + p.rows_per_block - 1) / p.rows_per_block;
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)blocks),
                                      dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess)
-        return QKR_ERR_HIP;
-    return hipGetLastError() == hipSuccess ? QKR_OK : QKR_ERR_HIP;
+    return err == hipSuccess ? QKR_OK : QKR_ERR_HIP;
 }

@@ -25,11 +25,14 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "host_common.h"
 #include "group_norm_silu.h"
 
 namespace {
 
 using namespace qkr_dev;
+using qkr_host::aligned16;
+using qkr_host::overlaps;
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
@@ -243,7 +246,7 @@ int launch(GnFn fn, int64_t blocks, const GnParams& p, hipStream_t stream)
     if (hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)blocks), dim3(kBlock),
                         args, 0, stream) != hipSuccess)
         return QKR_ERR_HIP;
-    return hipGetLastError() == hipSuccess ? QKR_OK : QKR_ERR_HIP;
+    return QKR_OK;
 }
 
 // Shape checks shared by the size query and the call; sets chunks and pairs.
@@ -266,7 +269,6 @@ int check_shape(int64_t n, int32_t channels, int64_t spatial, int32_t groups, in
     return QKR_OK;
 }
 
-bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 }  // namespace
 
@@ -302,13 +304,20 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
     if (!aligned16(x) || !aligned16(y) || !aligned16(gamma) || !aligned16(beta))
         return QKR_ERR_ALIGN;
     const int64_t gsize = (int64_t)(channels / groups) * spatial;
-    const uintptr_t bytes = (uintptr_t)(pairs * gsize) * 2u;
-    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
-    if (xa != ya && xa < ya + bytes && ya < xa + bytes)
+    const uint64_t bytes = (uint64_t)(pairs * gsize) * 2u;
+    const uint64_t param_bytes = (uint64_t)channels * (param_dtype == QKR_FP32 ? 4u : 2u);
+    // y is x itself or disjoint from it, and never overlaps gamma or beta
+    if ((x != y && overlaps(x, bytes, y, bytes)) || overlaps(y, bytes, gamma, param_bytes) ||
+        overlaps(y, bytes, beta, param_bytes))
         return QKR_ERR_ARG;
     const int64_t need = chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return QKR_ERR_WORKSPACE;
+    // the workspace is written too: apart from every other buffer
+    if (need > 0 && (overlaps(workspace, need, x, bytes) || overlaps(workspace, need, y, bytes) ||
+                     overlaps(workspace, need, gamma, param_bytes) ||
+                     overlaps(workspace, need, beta, param_bytes)))
+        return QKR_ERR_ARG;
 
     GnParams p;
     p.x = static_cast<const uint16_t*>(x);

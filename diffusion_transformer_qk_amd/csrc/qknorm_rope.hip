@@ -31,11 +31,14 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "host_common.h"
 #include "qknorm_rope.h"
 
 namespace {
 
 using namespace qkr_dev;
+using qkr_host::aligned16;
+using qkr_host::overlaps;
 
 constexpr int kInterleaved = QKR_ROPE_INTERLEAVED;
 constexpr int kRotateHalf = QKR_ROPE_ROTATE_HALF;
@@ -417,8 +420,6 @@ int check_config(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype, int32_
     return QKR_OK;
 }
 
-bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
-
 }  // namespace
 
 extern "C" int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, int32_t heads,
@@ -483,6 +484,26 @@ extern "C" int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, in
         if (!aligned16(p.gamma[s]))
             return QKR_ERR_ALIGN;
 
+    // The tensors written must not overlap each other or a read-only input.
+    const uint64_t tensor_bytes = (uint64_t)tokens * (uint64_t)hd * 2u;
+    const uint64_t table_bytes = (uint64_t)tokens * (uint64_t)head_dim *
+                                 (cos_layout == QKR_COS_PER_HEAD ? (uint64_t)heads : 1u) *
+                                 (cos_dtype == QKR_FP32 ? 4u : 2u);
+    const uint64_t gamma_bytes = (uint64_t)head_dim * 4u;
+    const void* written[2] = {qkv ? qkv : p.x[0], qkv ? nullptr : (p.n_tensors == 2 ? p.x[1] : nullptr)};
+    const uint64_t written_bytes = qkv ? 3 * tensor_bytes : tensor_bytes;
+    if (written[1] && overlaps(written[0], written_bytes, written[1], written_bytes))
+        return QKR_ERR_ARG;
+    for (const void* w : written) {
+        if (!w)
+            continue;
+        if (overlaps(w, written_bytes, cos, table_bytes) || overlaps(w, written_bytes, sin, table_bytes))
+            return QKR_ERR_ARG;
+        for (int s = 0; s < p.n_tensors; ++s)
+            if (overlaps(w, written_bytes, p.gamma[s], gamma_bytes))
+                return QKR_ERR_ARG;
+    }
+
     p.cos = cos;
     p.sin = sin;
     p.tokens = tokens;
@@ -495,9 +516,7 @@ extern "C" int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, in
     void* args[] = {&p};
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)l.blocks),
                                      dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess)
-        return QKR_ERR_HIP;
-    return hipGetLastError() == hipSuccess ? QKR_OK : QKR_ERR_HIP;
+    return err == hipSuccess ? QKR_OK : QKR_ERR_HIP;
 }
 
 extern "C" const char* qknorm_rope_strerror(int status)
@@ -505,12 +524,12 @@ extern "C" const char* qknorm_rope_strerror(int status)
     switch (status) {
     case QKR_OK: return "ok";
     case QKR_ERR_NULL: return "a required pointer is NULL";
-    case QKR_ERR_SHAPE: return "tokens or heads out of range";
+    case QKR_ERR_SHAPE: return "a size is out of range or the sizes do not fit together";
     case QKR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case QKR_ERR_UNSUPPORTED: return "unsupported size or dtype (head_dim 64/128; hidden or spatial a multiple of 8)";
     case QKR_ERR_MODE: return "pass either qkv, or q and/or k (not both, not neither)";
     case QKR_ERR_HIP: return "HIP launch or query failed";
-    case QKR_ERR_ARG: return "eps must be finite and > 0; enum argument out of range";
+    case QKR_ERR_ARG: return "eps not finite and > 0, an enum out of range, or a written buffer overlapping another";
     case QKR_ERR_WORKSPACE: return "workspace missing or smaller than required";
     default: return "unknown status";
     }

@@ -48,8 +48,9 @@ extern "C" {
  * stream          a hipStream_t (NULL = the default stream).
  *
  * Every pointer must be 16-byte aligned.  Returns QKR_OK or a negative
- * QKR_ERR_* code (QKR_ERR_ARG also when y partly overlaps x); all checks
- * happen before any HIP call and nothing is enqueued on error.
+ * QKR_ERR_* code (QKR_ERR_ARG also when y partly overlaps x, or overlaps scale
+ * or shift); all checks happen before any HIP call and nothing is enqueued on
+ * error.
  */
 int dit_fuse_scale_shift(const void* x, void* y, int64_t rows, int32_t hidden,
                          int64_t rows_per_batch, const void* scale, const void* shift,

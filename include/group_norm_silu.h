@@ -61,8 +61,9 @@ int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channels, int64_t 
  *
  * x, y, gamma and beta must be 16-byte aligned.  Returns QKR_OK or a negative
  * QKR_ERR_* code (QKR_ERR_WORKSPACE for a missing or short workspace,
- * QKR_ERR_ARG also when y partly overlaps x); all checks happen before any HIP
- * call and nothing is enqueued on error.
+ * QKR_ERR_ARG also when y partly overlaps x, y overlaps gamma or beta, or the
+ * workspace overlaps any other buffer); all checks happen before any HIP call
+ * and nothing is enqueued on error.
  */
 int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int64_t spatial,
                         int32_t groups, const void* gamma, const void* beta, int32_t param_dtype,

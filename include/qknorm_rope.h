@@ -44,7 +44,8 @@ enum {
     QKR_ERR_UNSUPPORTED = -4, /* head_dim not 64/128, or an unsupported dtype        */
     QKR_ERR_MODE = -5,        /* not exactly one of {qkv} / {q and/or k}             */
     QKR_ERR_HIP = -6,         /* the kernel launch (or an attribute query) failed     */
-    QKR_ERR_ARG = -7,         /* eps not finite and > 0, or an enum out of range      */
+    QKR_ERR_ARG = -7,         /* eps not finite and > 0, an enum out of range, or a   */
+                              /* buffer the call writes overlapping another buffer    */
     QKR_ERR_WORKSPACE = -8    /* workspace missing or smaller than required           */
 };
 
@@ -84,8 +85,10 @@ enum { QKR_ROPE_INTERLEAVED = 0, QKR_ROPE_ROTATE_HALF = 1 };
  * dtype       QKR_BF16 or QKR_FP16: element type of qkv / q / k.
  * stream      a hipStream_t (NULL = the default stream).
  *
- * Every data pointer must be 16-byte aligned.  Returns QKR_OK or a negative
- * QKR_ERR_* code; all checks happen before any HIP call.
+ * Every data pointer must be 16-byte aligned.  The tensors written (qkv, or q
+ * and k) must not overlap each other, gamma, cos or sin (QKR_ERR_ARG).
+ * Returns QKR_OK or a negative QKR_ERR_* code; all checks happen before any
+ * HIP call.
  */
 int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, int32_t heads,
                       int32_t head_dim, const float* q_gamma, const float* k_gamma, float eps,

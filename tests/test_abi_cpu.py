@@ -91,6 +91,32 @@ def test_rejects_before_any_hip_call(over, code):
     assert call(**over) == code
 
 
+T16 = 16 * 3 * 40 * 128 * 2          # bytes of the default call's fused QKV buffer
+Q16 = 16 * 40 * 128 * 2              # bytes of one separate [16, 40, 128] tensor
+G = 0x4000000                        # far from every buffer of the default call
+FAR = dict(cos=G, sin=G + 0x200000, q_gamma=G + 0x400000, k_gamma=G + 0x400000)
+
+
+@pytest.mark.parametrize("over", [
+    dict(cos=A + T16 - 16),                            # a table ends inside qkv
+    dict(sin=A + 4096),
+    dict(q_gamma=A + 1024),                            # a weight inside qkv (V region too)
+    dict(k_gamma=A + T16 - 16),
+    dict(qkv=0, q=A, k=A + Q16 - 16),                  # k starts inside q
+    dict(qkv=0, q=A + Q16 - 16, k=A),                  # q starts inside k
+    dict(qkv=0, q=A, k=A + Q16, cos=A + Q16 + 64),     # a table inside k
+    dict(qkv=0, k=A, k_gamma=A + 256),                 # k's weight inside k
+])
+def test_written_buffer_overlapping_another_is_rejected(over):
+    assert call(**{**FAR, **over}) == b.QKR_ERR_ARG
+
+
+def test_adjacent_buffers_pass_validation():
+    # adjacent, not overlapping: only the NULL table stops the call (nothing launched)
+    assert call(**{**FAR, "qkv": 0, "q": A, "k": A + Q16, "cos": 0}) == b.QKR_ERR_NULL
+    assert call(**{**FAR, "cos": A + T16, "sin": 0}) == b.QKR_ERR_NULL
+
+
 def test_zero_tokens_is_a_no_op():
     # valid scalars: OK without looking at (or launching on) the pointers
     assert call(tokens=0, qkv=0, q_gamma=0, k_gamma=0, cos=0, sin=0) == b.QKR_OK
@@ -147,6 +173,9 @@ def fss(**over):
     (dict(shift=MIS), b.QKR_ERR_ALIGN),
     (dict(y=A + 16 * 6144), b.QKR_ERR_ARG),        # y starts inside x
     (dict(x=A + 0x100000 + 1024 * 16, y=A + 0x100000), b.QKR_ERR_ARG),   # x inside y
+    (dict(scale=A + 0x100000 + 64), b.QKR_ERR_ARG),  # modulation inside y
+    (dict(x=A + 0x100000, y=A + 0x100000, shift=A + 0x100000 + 16 * 6144 * 2 - 16),
+     b.QKR_ERR_ARG),                               # in place, shift inside the buffer
 ])
 def test_fuse_scale_shift_rejects_before_any_hip_call(over, code):
     assert fss(**over) == code
@@ -208,6 +237,11 @@ def test_group_norm_workspace_size():
     (dict(spatial=65536), b.QKR_ERR_WORKSPACE),                # needs a workspace
     (dict(spatial=65536, workspace=A + 0x9000000, workspace_bytes=8), b.QKR_ERR_WORKSPACE),
     (dict(spatial=65536, workspace=MIS, workspace_bytes=1 << 20), b.QKR_ERR_WORKSPACE),
+    (dict(gamma=A + 0x1000000 + 64), b.QKR_ERR_ARG),                   # gamma inside y
+    (dict(x=A + 0x1000000, y=A + 0x1000000, beta=A + 0x1000000 + 4096), b.QKR_ERR_ARG),
+    (dict(spatial=65536, workspace=A + 0x1000000 + 64, workspace_bytes=1 << 20),
+     b.QKR_ERR_ARG),                                                   # workspace inside y
+    (dict(spatial=65536, workspace=A, workspace_bytes=1 << 20), b.QKR_ERR_ARG),  # inside x
 ])
 def test_group_norm_rejects_before_any_hip_call(over, code):
     assert gn(**over) == code
