@@ -39,32 +39,50 @@ if ROOT not in sys.path:
 
 METRIC = "QK-norm+RoPE µs/call and achieved HBM GB/s (% of peak), Wan 40×128 shape"
 PEAK_GBS = 8000.0            # MI355X HBM3E peak, GB/s
-KERNEL_SRCS = [os.path.join(ROOT, "diffusion_transformer_qk_amd", "csrc", name)
-               for name in ("qknorm_rope.hip", "device_common.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_headline.json")
+CSRC = os.path.join(ROOT, "diffusion_transformer_qk_amd", "csrc")
+# per step: the sources its kernels are built from (hashed, in order) and the
+# committed record of HBM bytes per launch measured with rocprofv3 counters
+KERNEL_SRCS = {
+    "qknorm_rope": [os.path.join(CSRC, n) for n in ("qknorm_rope.hip", "device_common.h")],
+    "fuse_scale_shift": [os.path.join(CSRC, n) for n in ("fuse_scale_shift.hip",
+                                                         "device_common.h")],
+    "group_norm_silu": [os.path.join(CSRC, n) for n in ("group_norm_silu.hip",
+                                                        "device_common.h")],
+}
+TRAFFIC_FILES = {
+    "qknorm_rope": os.path.join(ROOT, "profiles", "traffic_headline.json"),
+    "fuse_scale_shift": os.path.join(ROOT, "profiles", "traffic_adaln_wan.json"),
+    "group_norm_silu": os.path.join(ROOT, "profiles", "traffic_gn_vae_out.json"),
+}
+TRAFFIC_FILE = TRAFFIC_FILES["qknorm_rope"]
 
 
-def kernel_source_hash() -> str:
-    """SHA-256 (16 hex) over the QK-norm + RoPE kernel's sources, in order."""
+def kernel_source_hash(op: str = "qknorm_rope") -> str:
+    """SHA-256 (16 hex) over the sources of one step's kernels, in order."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[op]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, layout: str, style: str):
-    """HBM bytes per launch from committed rocprofv3 counters, if still current."""
+def recorded_traffic(path: str, op: str, key: str):
+    """HBM bytes per launch for run `key` from a counter record, if the record
+    was taken on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(op):
         return None
-    key = "%s/%s/%s" % (workload, layout, style)
     entry = rec.get("runs", {}).get(key)
     return None if entry is None else entry.get("bytes_per_launch")
+
+
+def measured_traffic(workload: str, layout: str, style: str):
+    """HBM bytes per launch of the QK-norm + RoPE kernel, if still current."""
+    return recorded_traffic(TRAFFIC_FILE, "qknorm_rope", "%s/%s/%s" % (workload, layout, style))
 
 
 def parse():
@@ -138,6 +156,79 @@ def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
             "sample": "%d whole passes over all %d tokens x %d Q+K heads (median pass), fp64 "
                       "C oracle with OpenMP, fp64 output in %d-token chunks"
                       % (len(passes), T, 2 * H, chunk)}
+
+
+def _cpu_passes(one_pass, budget_s):
+    """Run whole oracle passes until `budget_s` is spent (at least one, at
+    most 100); return (median seconds per pass, passes run)."""
+    import numpy as np
+    passes, spent = [], 0.0
+    while not passes or (spent < budget_s and len(passes) < 100):
+        t0 = time.perf_counter()
+        one_pass()
+        dt = time.perf_counter() - t0
+        passes.append(dt)
+        spent += dt
+    return float(np.median(passes)), len(passes)
+
+
+def cpu_baseline_adaln(x_cpu, w, sc, sh, mod_dtype, dtype, nbytes, budget_s):
+    """The fp64 oracle over every row of the AdaLN workload, in 2048-row chunks."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    bits = wl.u16(x_cpu)
+    scn = sc.numpy() if mod_dtype == "fp32" else wl.u16(sc)
+    shn = sh.numpy() if mod_dtype == "fp32" else wl.u16(sh)
+    chunk = 2048
+    out = np.empty((chunk, w.hidden), dtype=np.float64)
+
+    def one_pass():
+        for a in range(0, w.rows, chunk):
+            b = min(w.rows, a + chunk)
+            oracle.adaln(bits, dtype, hidden=w.hidden, rows_per_batch=w.rows_per_batch,
+                         scale=scn, shift=shn, mod_dtype=mod_dtype, eps=wl.EPS, row_begin=a,
+                         row_end=b, out=out[:b - a])
+
+    per_pass, n = _cpu_passes(one_pass, budget_s)
+    return {"value": round(nbytes / per_pass / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "ms_per_pass": round(per_pass * 1e3, 1),
+            "sample": "whole passes over all %d rows x %d: %d (median pass), fp64 C oracle "
+                      "with OpenMP, fp64 output in %d-row chunks" % (w.rows, w.hidden, n, chunk)}
+
+
+def cpu_baseline_gn(x_cpu, w, g, b, param_dtype, dtype, nbytes, budget_s):
+    """The fp64 oracle over every group of the group-norm workload, one group
+    at a time."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    bits = wl.u16(x_cpu)
+    gn = g.numpy() if param_dtype == "fp32" else wl.u16(g)
+    bn = b.numpy() if param_dtype == "fp32" else wl.u16(b)
+    gsize = w.channels // w.groups * w.spatial
+    pairs = w.n * w.groups
+    chunk = max(1, min(pairs, (1 << 28) // (8 * gsize)))      # <= 256 MB of fp64 output
+    out = np.empty(chunk * gsize, dtype=np.float64)
+
+    def one_pass():
+        for a in range(0, pairs, chunk):
+            b = min(pairs, a + chunk)
+            oracle.group_norm_silu(bits, dtype, channels=w.channels, spatial=w.spatial,
+                                   groups=w.groups, gamma=gn, beta=bn, param_dtype=param_dtype,
+                                   eps=wl.EPS, group_begin=a, group_end=b,
+                                   out=out[:(b - a) * gsize])
+
+    per_pass, n = _cpu_passes(one_pass, budget_s)
+    return {"value": round(nbytes / per_pass / 1e9, 3), "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "ms_per_pass": round(per_pass * 1e3, 1),
+            "sample": "whole passes over all %d groups of %d elements: %d (median pass), fp64 C "
+                      "oracle with OpenMP over groups, fp64 output %d groups at a time"
+                      % (pairs, gsize, n, chunk)}
 
 
 def time_launches(launch, stream, steps, warmup, flush_buf=None):
@@ -218,8 +309,15 @@ def bench_fuse_scale_shift(args):
         "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
         "bytes_per_call": nbytes, "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": recorded_traffic(
+                         TRAFFIC_FILES["fuse_scale_shift"], "fuse_scale_shift",
+                         "%s/%s/%s/%s" % (w.key, dtype, args.mod_dtype,
+                                          "inplace" if args.inplace else "out"))},
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_adaln(x_cpu, w, sc, sh, args.mod_dtype, dtype,
+                                                    nbytes, args.cpu_seconds)
     print(json.dumps(result))
     return 0
 
@@ -272,8 +370,15 @@ def bench_group_norm_silu(args):
         "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
         "bytes_per_call": nbytes, "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": recorded_traffic(
+                         TRAFFIC_FILES["group_norm_silu"], "group_norm_silu",
+                         "%s/%s/%s/%s" % (w.key, dtype, args.mod_dtype,
+                                          "inplace" if args.inplace else "out"))},
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_gn(x_cpu, w, g, b, args.mod_dtype, dtype, nbytes,
+                                                 args.cpu_seconds)
     print(json.dumps(result))
     return 0
 

@@ -29,3 +29,21 @@ def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch)
     with open(path, "w") as f:
         json.dump(rec, f)
     assert bench.measured_traffic("headline", "shared", "interleaved") is None
+
+
+import pytest  # noqa: E402
+
+
+@pytest.mark.parametrize("op,key", [("fuse_scale_shift", "adaln_wan/bf16/fp32/out"),
+                                    ("group_norm_silu", "gn_vae_out/bf16/fp32/out")])
+def test_step_traffic_records_follow_their_own_sources(tmp_path, op, key):
+    rec = {"kernel_source_sha256_16": bench.kernel_source_hash(op),
+           "runs": {key: {"bytes_per_launch": 77}}}
+    path = os.path.join(tmp_path, "t.json")
+    with open(path, "w") as f:
+        json.dump(rec, f)
+    assert bench.recorded_traffic(path, op, key) == 77
+    assert bench.recorded_traffic(path, op, key + "x") is None
+    other = "qknorm_rope" if op != "qknorm_rope" else "fuse_scale_shift"
+    assert bench.kernel_source_hash(other) != bench.kernel_source_hash(op)
+    assert bench.recorded_traffic(path, other, key) is None
