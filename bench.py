@@ -136,26 +136,59 @@ def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
     chunk = 2048
     out = np.empty((chunk, H, D), dtype=np.float64)
     c_np, s_np = cos.numpy(), sin.numpy()
-    passes, spent = [], 0.0
-    while not passes or (spent < budget_s and len(passes) < 100):
-        t0 = time.perf_counter()
-        for a in range(0, T, chunk):
-            b = min(T, a + chunk)
+    def tokens(a0, a1):
+        for a in range(a0, a1, chunk):
+            b = min(a1, a + chunk)
             for col0, g in ((0, qg), (H * D, kg)):
                 oracle.qknorm_rope(bits, dtype, row_stride=3 * H * D, col0=col0, heads=H,
                                    head_dim=D, gamma=g.numpy(), eps=wl.EPS, cos=c_np, sin=s_np,
                                    style=style, t_begin=a, t_end=b, out=out[:b - a])
-        dt = time.perf_counter() - t0
-        passes.append(dt)
-        spent += dt
-    per_pass = float(np.median(passes))
+
+    per_pass, n = _cpu_passes(lambda: tokens(0, T), budget_s)
     nbytes = wl.algorithmic_bytes(T, H, D)
+    sub = min(T, chunk)
+    one = _single_core(lambda: tokens(0, sub))
     return {"value": round(nbytes / per_pass / 1e9, 3), "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
             "ms_per_pass": round(per_pass * 1e3, 1),
-            "sample": "%d whole passes over all %d tokens x %d Q+K heads (median pass), fp64 "
+            "sample": "whole passes over all %d tokens x %d Q+K heads: %d (median pass), fp64 "
                       "C oracle with OpenMP, fp64 output in %d-token chunks"
-                      % (len(passes), T, 2 * H, chunk)}
+                      % (T, 2 * H, n, chunk),
+            "single_core": {"value": round(wl.algorithmic_bytes(sub, H, D) / one / 1e9, 3),
+                            "unit": "GB/s", "sample": "first %d tokens, median of 3" % sub},
+            **_host()}
+
+
+def _host():
+    """The host CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0))}
+
+
+def _single_core(sample_pass, reps=3):
+    """Median seconds of `sample_pass` with the oracle on one thread."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            sample_pass()
+            times.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_threads(threads)
+    return float(np.median(times))
 
 
 def _cpu_passes(one_pass, budget_s):
@@ -184,19 +217,24 @@ def cpu_baseline_adaln(x_cpu, w, sc, sh, mod_dtype, dtype, nbytes, budget_s):
     chunk = 2048
     out = np.empty((chunk, w.hidden), dtype=np.float64)
 
-    def one_pass():
-        for a in range(0, w.rows, chunk):
-            b = min(w.rows, a + chunk)
+    def rows(a0, a1):
+        for a in range(a0, a1, chunk):
+            b = min(a1, a + chunk)
             oracle.adaln(bits, dtype, hidden=w.hidden, rows_per_batch=w.rows_per_batch,
                          scale=scn, shift=shn, mod_dtype=mod_dtype, eps=wl.EPS, row_begin=a,
                          row_end=b, out=out[:b - a])
 
-    per_pass, n = _cpu_passes(one_pass, budget_s)
+    per_pass, n = _cpu_passes(lambda: rows(0, w.rows), budget_s)
+    sub = min(w.rows, chunk)
+    one = _single_core(lambda: rows(0, sub))
     return {"value": round(nbytes / per_pass / 1e9, 3), "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
             "ms_per_pass": round(per_pass * 1e3, 1),
             "sample": "whole passes over all %d rows x %d: %d (median pass), fp64 C oracle "
-                      "with OpenMP, fp64 output in %d-row chunks" % (w.rows, w.hidden, n, chunk)}
+                      "with OpenMP, fp64 output in %d-row chunks" % (w.rows, w.hidden, n, chunk),
+            "single_core": {"value": round(nbytes * sub / w.rows / one / 1e9, 3), "unit": "GB/s",
+                            "sample": "first %d rows, median of 3" % sub},
+            **_host()}
 
 
 def cpu_baseline_gn(x_cpu, w, g, b, param_dtype, dtype, nbytes, budget_s):
@@ -214,21 +252,25 @@ def cpu_baseline_gn(x_cpu, w, g, b, param_dtype, dtype, nbytes, budget_s):
     chunk = max(1, min(pairs, (1 << 28) // (8 * gsize)))      # <= 256 MB of fp64 output
     out = np.empty(chunk * gsize, dtype=np.float64)
 
-    def one_pass():
-        for a in range(0, pairs, chunk):
-            b = min(pairs, a + chunk)
+    def groups(a0, a1):
+        for a in range(a0, a1, chunk):
+            b = min(a1, a + chunk)
             oracle.group_norm_silu(bits, dtype, channels=w.channels, spatial=w.spatial,
                                    groups=w.groups, gamma=gn, beta=bn, param_dtype=param_dtype,
                                    eps=wl.EPS, group_begin=a, group_end=b,
                                    out=out[:(b - a) * gsize])
 
-    per_pass, n = _cpu_passes(one_pass, budget_s)
+    per_pass, n = _cpu_passes(lambda: groups(0, pairs), budget_s)
+    one = _single_core(lambda: groups(0, 1))
     return {"value": round(nbytes / per_pass / 1e9, 3), "unit": "GB/s",
             "cores": oracle.max_threads(), "kind": "oracle",
             "ms_per_pass": round(per_pass * 1e3, 1),
             "sample": "whole passes over all %d groups of %d elements: %d (median pass), fp64 C "
                       "oracle with OpenMP over groups, fp64 output %d groups at a time"
-                      % (pairs, gsize, n, chunk)}
+                      % (pairs, gsize, n, chunk),
+            "single_core": {"value": round(nbytes / pairs / one / 1e9, 3), "unit": "GB/s",
+                            "sample": "first group, median of 3"},
+            **_host()}
 
 
 def time_launches(launch, stream, steps, warmup, flush_buf=None):

@@ -82,11 +82,17 @@ class Oracle:
         lib.qkr_oracle_group_norm_silu.restype = c_int
         lib.qkr_oracle_max_threads.argtypes = []
         lib.qkr_oracle_max_threads.restype = c_int
+        lib.qkr_oracle_set_threads.argtypes = [c_int]
+        lib.qkr_oracle_set_threads.restype = None
         self.lib = lib
         self.path = lib_path
 
     def max_threads(self) -> int:
         return int(self.lib.qkr_oracle_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads for the following calls (for single-core timing)."""
+        self.lib.qkr_oracle_set_threads(int(n))
 
     def decode(self, bits: np.ndarray, dtype: str) -> np.ndarray:
         """Exact fp64 values of bf16/fp16 bit patterns (uint16 array)."""
@@ -229,6 +235,10 @@ def default() -> Oracle:
 
 def max_threads() -> int:
     return default().max_threads()
+
+
+def set_threads(n: int) -> None:
+    default().set_threads(n)
 
 
 def decode(bits, dtype):

@@ -333,3 +333,16 @@ int qkr_oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the next oracle calls use (n >= 1); for timing the oracle on one
+ * core beside all cores. */
+void qkr_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

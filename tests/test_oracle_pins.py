@@ -454,3 +454,23 @@ def test_rejects_bad_arguments(oracle_lib):
         oracle_lib.qknorm_rope(np.zeros((2, 64), np.uint16), "bf16", row_stride=64, col0=0,
                                heads=0, head_dim=64, gamma=np.ones(64, np.float32), eps=1e-6,
                                cos=c, sin=s, t_begin=0, t_end=2)
+
+
+def test_thread_count_does_not_change_results(oracle_lib):
+    """Every output element is computed by one thread from its own row, so the
+    oracle's bits do not depend on how many threads run (the bench times it
+    on one core and on all)."""
+    T, H, D = 37, 3, 64
+    qkv = wl.fused_qkv(71, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(71, D)
+    cos, sin = wl.rope_tables(np.arange(T), (D // 2,), D, "interleaved")
+    args = dict(heads=H, head_dim=D, q_gamma=qg.numpy(), k_gamma=kg.numpy(), eps=wl.EPS,
+                cos=cos.numpy(), sin=sin.numpy(), style="interleaved")
+    many = oracle_lib.fused_qk(wl.u16(qkv), "bf16", **args)
+    threads = oracle_lib.max_threads()
+    oracle_lib.set_threads(1)
+    try:
+        one = oracle_lib.fused_qk(wl.u16(qkv), "bf16", **args)
+    finally:
+        oracle_lib.set_threads(threads)
+    assert all(np.array_equal(a, b) for a, b in zip(many, one))
