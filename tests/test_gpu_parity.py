@@ -186,7 +186,8 @@ def test_mid_workload_and_layout_parity():
     qg, kg = wl.norm_weights(w.seed, D)
     cos, sin = wl.workload_tables(w, "rotate_half")
     shared = run_fused(qkv, qg, kg, cos, sin, "rotate_half")
-    compare_fused(shared, qkv, "bf16", H, D, qg, kg, cos, sin, "rotate_half", what="mid")
+    m = compare_fused(shared, qkv, "bf16", H, D, qg, kg, cos, sin, "rotate_half", what="mid")
+    print("mid max_abs", m)
     per_head = run_fused(qkv, qg, kg, wl.expand_per_head(cos, H), wl.expand_per_head(sin, H),
                          "rotate_half", layout="per_head")
     assert torch.equal(shared.view(torch.int16), per_head.view(torch.int16))
