@@ -6,23 +6,24 @@
 // implemented is the plain AdaLN one (see include/fuse_scale_shift.h).
 //
 // Work mapping (memory-bound, no matrix cores):
-//   * a 256-thread workgroup owns a contiguous run of rows and handles them
-//     one at a time: thread j holds vectors j, j+256, ... of the row (8
-//     elements each, 16-byte non-temporal loads), VPT vectors per thread, so
-//     each load instruction of the workgroup reads one contiguous 4 KB and the
-//     whole row sits in registers; the loads of the next two rows are in
-//     flight while the current row is reduced;
-//   * the modulation vectors (scale and shift, the same channels as the
-//     thread's row vectors) stay in registers across the run and are reloaded
-//     only when the batch changes, so they cost L2 traffic once per run, not
-//     once per row.  Spreading a row over a workgroup rather than a wave keeps
-//     these registers small (hidden * 2 tables * bytes / 256 threads);
+//   * one wave per row: lane j holds the row's 16-byte vectors j, j+64, ...
+//     (VPT of them, 8 elements each), loaded non-temporally with buffer
+//     loads whose range is the row, so vectors past the row end read as zero
+//     and their stores are dropped (no clamped addressing); each load
+//     instruction of the wave reads one contiguous 1 KB;
 //   * two passes over the registers: the sum (mean), then the sum of squared
-//     deviations (biased variance).  Each is reduced in the wave with DPP
-//     inside 16-lane rows and two lane swaps, then across the 4 waves through
-//     LDS in a fixed order, so every thread holds the same bits;
+//     deviations (biased variance); each is reduced inside the wave only
+//     (DPP within 16-lane rows, then the four row totals read as scalars and
+//     added as (r0 + r1) + (r2 + r3)), so no workgroup barrier sits between a
+//     row's loads and its stores;
+//   * modulation: for large calls a workgroup of 4 waves (4 consecutive rows)
+//     first stages the scale and shift rows of its first row's batch in LDS
+//     (the rows' loads are already in flight) and every wave whose row is in
+//     that batch reads them from there; for small calls (a grid that fits
+//     the chip at once) each wave is its own workgroup and reads them from
+//     L2, which keeps every row's loads in flight without a staging step;
 //   * y = fma((x - mean) * rsqrt(var + eps), 1 + scale, shift), packed with
-//     the round-to-nearest-even converts and stored non-temporally.
+//     the round-to-nearest-even converts, stored non-temporally.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -38,8 +39,8 @@ using namespace qkr_dev;
 using qkr_host::aligned16;
 using qkr_host::overlaps;
 
-constexpr int kWaves = 4;
-constexpr int kBlock = kWaves * kWave;   // one row per workgroup
+constexpr int kBufferNT = 2;                     // buffer cache policy bits: non-temporal
+constexpr uint32_t kBufferFlags = 0x00020000u;   // raw buffer resource, 32-bit data
 
 struct FssParams {
     const uint16_t* x;
@@ -48,13 +49,15 @@ struct FssParams {
     const void* shift;
     int64_t rows;
     int64_t rows_per_batch;
-    int64_t rows_per_block;    // length of each workgroup's run of rows
     int32_t hidden;
     float eps;
 };
 
 template <int MOD>
 constexpr int mod_vecs() { return MOD == QKR_FP32 ? 2 : 1; }   // 16-byte vectors per 8 entries
+
+template <int MOD>
+constexpr int mod_bytes() { return MOD == QKR_FP32 ? 4 : 2; }
 
 template <int MOD>
 __device__ __forceinline__ void widen_mod(const u32x4* w, float f[8])
@@ -70,169 +73,218 @@ __device__ __forceinline__ void widen_mod(const u32x4* w, float f[8])
     }
 }
 
-// Issue the row's VPT vector loads; vectors past the row end load the last
-// vector again (clamped index, so every load is valid and unconditional) and
-// are zeroed by the caller's mask.
-template <int VPT>
-__device__ __forceinline__ void load_row(const uint16_t* xr, int nvec, u32x4 (&v)[VPT])
+// Sum over the wave; every lane gets the same bits.
+__device__ __forceinline__ float wave_total(float v)
 {
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int i = u * kBlock + threadIdx.x;
-        v[u] = load16<true>(xr + (i < nvec ? i : nvec - 1) * kVec);
-    }
+    v += dpp<0xB1>(v);      // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);      // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);     // row_half_mirror
+    v += dpp<0x140>(v);     // row_mirror: each 16-lane row's total in all its lanes
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
-template <int VPT, int MOD, int NV>
-__device__ __forceinline__ void load_mods(const FssParams& p, int64_t mrow, int nvec,
-                                          u32x4 (&sc)[VPT * NV], u32x4 (&sh)[VPT * NV])
+// Make the compiler forget what v holds, so the fp32 values unpacked from it
+// are unpacked again for each pass instead of being kept alive across them.
+template <int VPT>
+__device__ __forceinline__ void forget_unpacked(u32x4 (&v)[VPT])
 {
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int i = u * kBlock + threadIdx.x;
-        const int ic = i < nvec ? i : nvec - 1;
+    for (int u = 0; u < VPT; ++u)
+        __asm__ volatile("" : "+v"(v[u]));
+}
+
+// Vector i (8 entries) of a modulation row, from LDS (staged as 16-byte
+// vectors: scale at [0, nvec * NV), shift after it) or from global memory.
+template <int MOD, bool FROM_LDS>
+__device__ __forceinline__ void mod_entries(const FssParams& p, const u32x4* staged, int nvec,
+                                            int64_t mrow, int i, float s[8], float h[8])
+{
+    constexpr int NV = mod_vecs<MOD>();
+    u32x4 ws[NV], wh[NV];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int64_t e = mrow + ic * kVec + k * 4;
+    for (int k = 0; k < NV; ++k) {
+        if constexpr (FROM_LDS) {
+            ws[k] = staged[i * NV + k];
+            wh[k] = staged[nvec * NV + i * NV + k];
+        } else {
+            const int64_t e = mrow + (int64_t)i * kVec + k * 4;   // entries
             if constexpr (MOD == QKR_FP32) {
-                sc[u * NV + k] = load16<false>(static_cast<const float*>(p.scale) + e);
-                sh[u * NV + k] = load16<false>(static_cast<const float*>(p.shift) + e);
+                ws[k] = load16<false>(static_cast<const float*>(p.scale) + e);
+                wh[k] = load16<false>(static_cast<const float*>(p.shift) + e);
             } else {
-                sc[u * NV + k] = load16<false>(static_cast<const uint16_t*>(p.scale) + e);
-                sh[u * NV + k] = load16<false>(static_cast<const uint16_t*>(p.shift) + e);
+                ws[k] = load16<false>(static_cast<const uint16_t*>(p.scale) + e);
+                wh[k] = load16<false>(static_cast<const uint16_t*>(p.shift) + e);
             }
         }
     }
+    widen_mod<MOD>(ws, s);
+    widen_mod<MOD>(wh, h);
 }
 
-// AHEAD: rows whose loads are in flight beyond the one being reduced (1 or 2).
-template <int VPT, bool X_FP16, int MOD, int AHEAD>
-__global__ __launch_bounds__(kBlock) void fuse_scale_shift_kernel(const FssParams p)
+template <int VPT, bool X_FP16, int MOD, bool FROM_LDS, bool FULL>
+__device__ __forceinline__ void modulate_store(const FssParams& p, __amdgpu_buffer_rsrc_t yr,
+                                               const u32x4 (&v)[VPT], const u32x4* staged, int nvec,
+                                               int64_t mrow, float mean, float rstd)
+{
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kWave + lane;
+        if (FULL || i < nvec) {
+            float f[8], s[8], h[8], o[8];
+            unpack8<X_FP16>(v[u], f);
+            mod_entries<MOD, FROM_LDS>(p, staged, nvec, mrow, i, s, h);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                o[k] = __builtin_fmaf((f[k] - mean) * rstd, 1.0f + s[k], h[k]);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8<X_FP16>(o), yr, i * 16, 0, kBufferNT);
+        }
+    }
+}
+
+// WAVES == 1: one row per workgroup, modulation from L2.  WAVES > 1: WAVES
+// consecutive rows per workgroup, the first row's batch staged in LDS.
+// FULL: the row is exactly VPT vectors per lane (hidden = 512 * VPT), so no
+// lane needs the row-end masks (a masked store costs an exec-mask branch per
+// vector, measured at 3% on 32760 x 5120).
+template <int VPT, bool X_FP16, int MOD, int WAVES, bool FULL>
+__global__ __launch_bounds__(WAVES * kWave) void fuse_scale_shift_kernel(const FssParams p)
 {
     constexpr int NV = mod_vecs<MOD>();
-    __shared__ float red[2][kWaves];
-    const int tid = threadIdx.x;
+    extern __shared__ u32x4 staged[];        // WAVES > 1: [2][nvec * NV]
+    const int lane = threadIdx.x % kWave;
     const int C = p.hidden;
     const int nvec = C / kVec;
-    const int64_t r0 = (int64_t)blockIdx.x * p.rows_per_block;
-    const int64_t r1 = r0 + p.rows_per_block < p.rows ? r0 + p.rows_per_block : p.rows;
+    const int64_t first = (int64_t)blockIdx.x * WAVES;
+    // the wave's row, made visibly wave-uniform so the buffer resources built
+    // from it live in scalar registers
+    const int64_t r = first + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool active = r < p.rows;
+    const int row_bytes = C * 2;
 
-    u32x4 v[VPT], vn[VPT], vnn[VPT], sc[VPT * NV], sh[VPT * NV];
-    load_row<VPT>(p.x + r0 * C, nvec, v);
-    if (AHEAD > 1 && r0 + 1 < r1)
-        load_row<VPT>(p.x + (r0 + 1) * C, nvec, vn);
-    int64_t batch = r0 / p.rows_per_batch;
-    load_mods<VPT, MOD, NV>(p, batch * C, nvec, sc, sh);
-
-    for (int64_t r = r0; r < r1; ++r) {
-        if (AHEAD > 1) {
-            if (r + 2 < r1)
-                load_row<VPT>(p.x + (r + 2) * C, nvec, vnn);
-        } else if (r + 1 < r1) {
-            load_row<VPT>(p.x + (r + 1) * C, nvec, vn);
-        }
+    // the row's loads first: nothing they need waits on the staging below
+    u32x4 v[VPT];
+    if (active) {
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.x + r * C), 0, row_bytes, kBufferFlags);
 #pragma unroll
         for (int u = 0; u < VPT; ++u)
-            if (u * kBlock + tid >= nvec)
-                v[u] = u32x4{0, 0, 0, 0};
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, (u * kWave + lane) * 16, 0, kBufferNT);
+    }
+    const int64_t staged_batch = first / p.rows_per_batch;
+    if constexpr (WAVES > 1) {
+        const char* sc = static_cast<const char*>(p.scale) + staged_batch * C * mod_bytes<MOD>();
+        const char* sh = static_cast<const char*>(p.shift) + staged_batch * C * mod_bytes<MOD>();
+        for (int i = threadIdx.x; i < nvec * NV; i += WAVES * kWave) {
+            staged[i] = load16<false>(sc + i * 16);
+            staged[nvec * NV + i] = load16<false>(sh + i * 16);
+        }
+        __syncthreads();
+    }
+    if (!active)
+        return;
 
-        // pass 1: mean (vectors past the row end hold zeros and add nothing)
-        float sum = 0.0f;
+    // pass 1: mean (vectors past the row end read as zero and add nothing)
+    float sum = 0.0f;
 #pragma unroll
-        for (int u = 0; u < VPT; ++u) {
+    for (int u = 0; u < VPT; ++u) {
+        float f[8];
+        unpack8<X_FP16>(v[u], f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            sum += f[k];
+    }
+    const float mean = wave_total(sum) / (float)C;
+    forget_unpacked(v);
+
+    // pass 2: biased variance from the deviations (row vectors only)
+    float ss = 0.0f;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        if (FULL || u * kWave + lane < nvec) {
             float f[8];
             unpack8<X_FP16>(v[u], f);
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                sum += f[k];
-        }
-        const float mean = block_sum<kWaves>(sum, red[0]) / (float)C;
-
-        // pass 2: biased variance from the deviations
-        float ss = 0.0f;
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            if (u * kBlock + tid < nvec) {
-                float f[8];
-                unpack8<X_FP16>(v[u], f);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float d = f[k] - mean;
-                    ss = __builtin_fmaf(d, d, ss);
-                }
+            for (int k = 0; k < 8; ++k) {
+                const float d = f[k] - mean;
+                ss = __builtin_fmaf(d, d, ss);
             }
-        }
-        const float rstd = __builtin_amdgcn_rsqf(block_sum<kWaves>(ss, red[1]) / (float)C + p.eps);
-
-        // the row's batch (uniform over the workgroup): reload its modulation
-        const int64_t b = r / p.rows_per_batch;
-        if (b != batch) {
-            batch = b;
-            load_mods<VPT, MOD, NV>(p, batch * C, nvec, sc, sh);
-        }
-
-        // pass 3: normalise, modulate, round, store
-        uint16_t* yr = p.y + r * C;
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int i = u * kBlock + tid;
-            if (i < nvec) {
-                float f[8], s[8], h[8], o[8];
-                unpack8<X_FP16>(v[u], f);
-                widen_mod<MOD>(&sc[u * NV], s);
-                widen_mod<MOD>(&sh[u * NV], h);
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    o[k] = __builtin_fmaf((f[k] - mean) * rstd, 1.0f + s[k], h[k]);
-                store16<true>(yr + i * kVec, pack8<X_FP16>(o));
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            v[u] = vn[u];
-            if (AHEAD > 1)
-                vn[u] = vnn[u];
         }
     }
+    const float rstd = __builtin_amdgcn_rsqf(wave_total(ss) / (float)C + p.eps);
+    forget_unpacked(v);
+
+    // pass 3: normalise, modulate, round, store
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(p.y + r * C, 0, row_bytes, kBufferFlags);
+    const int64_t batch = r / p.rows_per_batch;
+    if (WAVES > 1 && batch == staged_batch)
+        modulate_store<VPT, X_FP16, MOD, true, FULL>(p, yr, v, staged, nvec, 0, mean, rstd);
+    else
+        modulate_store<VPT, X_FP16, MOD, false, FULL>(p, yr, v, staged, nvec, batch * C, mean,
+                                                      rstd);
 }
 
 using FssFn = void (*)(FssParams);
 
-constexpr int kRowsAhead = 2;
+// Rows from which workgroups of 4 rows stage the modulation in LDS; below it
+// one-row workgroups read it from L2 (measured on 32760 x 5120 and
+// 4608 x 6144: staging wins at the first by 20%, loses at the second by 23%).
+constexpr int64_t kStageFromRows = 16384;
+constexpr int kStageWaves = 4;
 
-template <int VPT, bool XF>
+template <int VPT, bool XF, int WAVES, bool FULL>
 FssFn select_mod(int mod)
 {
     if (mod == QKR_FP32)
-        return fuse_scale_shift_kernel<VPT, XF, QKR_FP32, kRowsAhead>;
+        return fuse_scale_shift_kernel<VPT, XF, QKR_FP32, WAVES, FULL>;
     if (mod == QKR_FP16)
-        return fuse_scale_shift_kernel<VPT, XF, QKR_FP16, kRowsAhead>;
-    return fuse_scale_shift_kernel<VPT, XF, QKR_BF16, kRowsAhead>;
+        return fuse_scale_shift_kernel<VPT, XF, QKR_FP16, WAVES, FULL>;
+    return fuse_scale_shift_kernel<VPT, XF, QKR_BF16, WAVES, FULL>;
+}
+
+template <int VPT, bool XF, bool FULL>
+FssFn select_waves(int waves, int mod)
+{
+    return waves > 1 ? select_mod<VPT, XF, kStageWaves, FULL>(mod) : select_mod<VPT, XF, 1, FULL>(mod);
 }
 
 template <int VPT>
-FssFn select_x(bool xf, int mod) { return xf ? select_mod<VPT, true>(mod) : select_mod<VPT, false>(mod); }
-
-// Row vectors per thread: ceil(hidden / 8 / 256), 1..4 for hidden <= 8192.
-int vectors_per_thread(int hidden) { return (hidden / kVec + kBlock - 1) / kBlock; }
-
-FssFn select_kernel(int vpt, bool xf, int mod)
+FssFn select_x(bool xf, bool full, int waves, int mod)
 {
-    switch (vpt) {
-    case 1: return select_x<1>(xf, mod);
-    case 2: return select_x<2>(xf, mod);
-    case 3: return select_x<3>(xf, mod);
-    default: return select_x<4>(xf, mod);
-    }
+    if (full)
+        return xf ? select_waves<VPT, true, true>(waves, mod) : select_waves<VPT, false, true>(waves, mod);
+    return xf ? select_waves<VPT, true, false>(waves, mod) : select_waves<VPT, false, false>(waves, mod);
 }
 
-// Rows per workgroup: runs of 3 rows (loads two rows ahead) amortise the
-// modulation loads and still leave about 11000 workgroups on a 32K-row call;
-// shorter runs for small calls keep the grid large enough to fill the chip
-// (measured over 1..32 rows per workgroup and 1..2 rows ahead on 32760 x 5120
-// and 4608 x 6144).
-int64_t rows_per_block(int64_t rows) { return rows >= 16384 ? 3 : rows >= 4096 ? 2 : 1; }
+// Row vectors per lane: ceil(hidden / 8 / 64) rounded up to an even count,
+// 2..16 for hidden <= 8192 (the extra vectors of a rounded-up count read as
+// zero and store nothing).
+int vectors_per_lane(int hidden)
+{
+    const int v = (hidden / kVec + kWave - 1) / kWave;
+    return v + (v & 1);
+}
 
+FssFn select_kernel(int hidden, bool xf, int waves, int mod)
+{
+    const int vpl = vectors_per_lane(hidden);
+    const bool full = hidden == vpl * kWave * kVec;
+    switch (vpl) {
+    case 2: return select_x<2>(xf, full, waves, mod);
+    case 4: return select_x<4>(xf, full, waves, mod);
+    case 6: return select_x<6>(xf, full, waves, mod);
+    case 8: return select_x<8>(xf, full, waves, mod);
+    case 10: return select_x<10>(xf, full, waves, mod);
+    case 12: return select_x<12>(xf, full, waves, mod);
+    case 14: return select_x<14>(xf, full, waves, mod);
+    default: return select_x<16>(xf, full, waves, mod);
+    }
+}
 
 }  // namespace
 
@@ -271,13 +323,16 @@ extern "C" int dit_fuse_scale_shift(const void* x, void* y, int64_t rows, int32_
     p.shift = shift;
     p.rows = rows;
     p.rows_per_batch = rows_per_batch;
-    p.rows_per_block = rows_per_block(rows);
     p.hidden = hidden;
     p.eps = eps;
-    FssFn fn = select_kernel(vectors_per_thread(hidden), dtype == QKR_FP16, mod_dtype);
+    const int waves = rows >= kStageFromRows ? kStageWaves : 1;
+    FssFn fn = select_kernel(hidden, dtype == QKR_FP16, waves, mod_dtype);
+    // staged scale and shift rows: 2 * hidden * 4 bytes at most (64 KB at 8192)
+    const size_t lds = waves > 1 ? (size_t)2 * hidden * (mod_dtype == QKR_FP32 ? 4 : 2) : 0;
     void* args[] = {&p};
-    const int64_t blocks = (rows + p.rows_per_block - 1) / p.rows_per_block;
+    const int64_t blocks = (rows + waves - 1) / waves;
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)blocks),
-                                     dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
+                                     dim3(waves * kWave), args, lds,
+                                     static_cast<hipStream_t>(stream));
     return err == hipSuccess ? QKR_OK : QKR_ERR_HIP;
 }

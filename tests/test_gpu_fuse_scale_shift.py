@@ -1,5 +1,10 @@
 """GPU parity of the AdaLN modulation (dit_fuse_scale_shift) against the fp64 oracle.
 
+Calls of 16384 rows or more run workgroups of 4 rows that stage the
+modulation in LDS; smaller calls run one-row workgroups that read it from L2.
+Both schedules are covered, including rows whose batch differs from the one
+their workgroup staged.
+
 Bar (no fixed tolerance is given for this step, so it follows from the
 arithmetic): every output within half an ulp of the exact value plus fp32
 noise, the noise bounded by 8e-6 times the largest term |n (1 + scale)| +
@@ -214,3 +219,27 @@ def test_byte_offsets_beyond_4gib_in_place():
     m = check_rows(_decode(x[idx.to(DEV)], "bf16"), y, n, sc, sh, len(samples), 0, "bf16",
                    ">4GiB rows")
     print("beyond 4 GiB max_abs", m)
+
+
+@pytest.mark.parametrize("rows,hidden,rpb,mod", [
+    (16390, 512, 4097, "fp32"),      # staged; workgroups straddle every batch boundary
+    (16387, 64, 5, "bf16"),          # staged; most rows outside the staged batch
+    (16384, 8192, 16384, "fp32"),    # staged 64 KB of modulation, widest rows
+    (16400, 5128, 8200, "fp16"),     # staged, a row tail (641 vectors)
+    (16383, 5128, 8191, "fp32"),     # one below the staging threshold, same tail
+    (300, 8, 7, "fp32"),             # one vector per row
+])
+def test_staging_schedules_and_tails(rows, hidden, rpb, mod):
+    batches = -(-rows // rpb)
+    x, sc, sh = wl.adaln_inputs(rows + hidden, rows, hidden, batches, "bf16", mod)
+    out = run(x, sc, sh, rows_per_batch=rpb)
+    rng = np.random.default_rng(rows)
+    edges = sorted({b * rpb + d for b in range(1, batches) for d in (-3, -1, 0, 2)} |
+                   set(rng.integers(0, rows, 6).tolist()) | {0, rows - 1})
+    worst = 0.0
+    for a in edges:
+        a = max(0, min(a, rows - 4))
+        y, n = oracle_rows(x, "bf16", sc, sh, rpb, wl.EPS, a, a + 4)
+        worst = max(worst, check_rows(_decode(out[a:a + 4], "bf16"), y, n, sc, sh, rpb, a, "bf16",
+                                      "rows %d:%d" % (a, a + 4)))
+    print("staging", rows, hidden, rpb, mod, "max_abs", worst)
