@@ -268,9 +268,11 @@ void fuse_scale_shift_kernel(const FssParams p)
 using FssFn = void (*)(FssParams);
 
 // Rows from which workgroups of 4 rows stage the modulation in LDS; below it
-// one-row workgroups read it from L2 (measured on 32760 x 5120 and
-// 4608 x 6144: staging wins at the first by 20%, loses at the second by 23%).
-constexpr int64_t kStageFromRows = 16384;
+// one-row workgroups read it from L2.  Measured at widths 5120 and 6144: the
+// one-row schedule wins up to about 6000 rows (23.0 vs 26.0 us at 6144 x 5120,
+// 17.5 vs 26 us at 4608 x 6144), staging wins from 8192 rows on (33.7 vs
+// 41.1 us at 8192 x 5120, 116 vs 143 us at 32760 x 5120).
+constexpr int64_t kStageFromRows = 8192;
 constexpr int kStageWaves = 4;
 
 template <int VPT, bool XF, int WAVES, bool FULL>

@@ -1,6 +1,6 @@
 """GPU parity of the AdaLN modulation (dit_fuse_scale_shift) against the fp64 oracle.
 
-Calls of 16384 rows or more run workgroups of 4 rows that stage the
+Calls of 8192 rows or more run workgroups of 4 rows that stage the
 modulation in LDS; smaller calls run one-row workgroups that read it from L2.
 Both schedules are covered, including rows whose batch differs from the one
 their workgroup staged.
@@ -223,10 +223,10 @@ def test_byte_offsets_beyond_4gib_in_place():
 
 @pytest.mark.parametrize("rows,hidden,rpb,mod", [
     (16390, 512, 4097, "fp32"),      # staged; workgroups straddle every batch boundary
-    (16387, 64, 5, "bf16"),          # staged; most rows outside the staged batch
-    (16384, 8192, 16384, "fp32"),    # staged 64 KB of modulation, widest rows
-    (16400, 5128, 8200, "fp16"),     # staged, a row tail (641 vectors)
-    (16383, 5128, 8191, "fp32"),     # one below the staging threshold, same tail
+    (8195, 64, 5, "bf16"),           # staged; most rows outside the staged batch
+    (8192, 8192, 8192, "fp32"),      # staged 64 KB of modulation, widest rows
+    (8200, 5128, 4100, "fp16"),      # staged, a row tail (641 vectors)
+    (8191, 5128, 4095, "fp32"),      # one below the staging threshold, same tail
     (300, 8, 7, "fp32"),             # one vector per row
 ])
 def test_staging_schedules_and_tails(rows, hidden, rpb, mod):
