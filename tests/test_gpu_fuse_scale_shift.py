@@ -243,3 +243,50 @@ def test_staging_schedules_and_tails(rows, hidden, rpb, mod):
         worst = max(worst, check_rows(_decode(out[a:a + 4], "bf16"), y, n, sc, sh, rpb, a, "bf16",
                                       "rows %d:%d" % (a, a + 4)))
     print("staging", rows, hidden, rpb, mod, "max_abs", worst)
+
+
+@pytest.mark.parametrize("rows", [300, 9000])      # one-row and staging schedules
+def test_graph_capture_replays_match_eager(rows):
+    """The call holds no allocation, copy or synchronisation: captured into a
+    graph, every replay (with eager work and synchronisation between them)
+    equals the eager result bit for bit."""
+    hidden = 1024
+    x, sc, sh = wl.adaln_inputs(rows, rows, hidden, 3, "bf16", "fp32")
+    xd, scd, shd = x.to(DEV), sc.to(DEV), sh.to(DEV)
+    rpb = -(-rows // 3)
+    eager = qkr.fuse_scale_shift(xd, scd, shd, rows_per_batch=rpb)
+    out = torch.empty_like(xd)
+    st = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=st):
+        qkr.fuse_scale_shift(xd, scd, shd, out=out, rows_per_batch=rpb)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), replay
+
+
+def test_concurrent_streams_are_independent():
+    """Calls on four streams over different buffers, both schedules, at once."""
+    cases = []
+    for i in range(4):
+        rows = (300, 9000)[i % 2]
+        x, sc, sh = wl.adaln_inputs(500 + i, rows, 2048, 1, "fp16", "bf16")
+        cases.append((x, sc, sh, x.to(DEV), sc.to(DEV), sh.to(DEV), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    outs = []
+    for x, sc, sh, xd, scd, shd, st in cases:
+        with torch.cuda.stream(st):
+            outs.append(qkr.fuse_scale_shift(xd, scd, shd, stream=st))
+    torch.cuda.synchronize()
+    for (x, sc, sh, *_), out in zip(cases, outs):
+        rows = x.shape[0]
+        y, n = oracle_rows(x, "fp16", sc, sh, rows, wl.EPS, 0, 64)
+        check_rows(_decode(out[:64], "fp16"), y, n, sc, sh, rows, 0, "fp16", "stream")
+        y, n = oracle_rows(x, "fp16", sc, sh, rows, wl.EPS, rows - 64, rows)
+        check_rows(_decode(out[rows - 64:], "fp16"), y, n, sc, sh, rows, rows - 64, "fp16",
+                   "stream tail")

@@ -262,3 +262,21 @@ def test_byte_offsets_beyond_4gib_in_place():
                             q % (B * groups), q % (B * groups) + 1)
         got = _decode(flat[q * gsize:(q + 1) * gsize], "bf16")
         check_groups(got, ref, gsize, "bf16", ">4GiB group %d" % q)
+
+
+def test_concurrent_streams_are_independent():
+    """Group-norm calls on four streams (own workspaces) at once."""
+    cases = []
+    for i in range(4):
+        n, channels, spatial, groups = 1, 32, (64 * 64, 256 * 256)[i % 2], 4
+        x, g, b = wl.gn_inputs(600 + i, n, channels, spatial, "bf16", "fp32")
+        cases.append((x, g, b, spatial, x.to(DEV), g.to(DEV), b.to(DEV), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    outs = []
+    for x, g, b, spatial, xd, gd, bd, st in cases:
+        with torch.cuda.stream(st):
+            outs.append(qkr.group_norm_silu(xd, gd, bd, 4, stream=st))
+    torch.cuda.synchronize()
+    for (x, g, b, spatial, *_), out in zip(cases, outs):
+        ref = oracle_groups(x, "bf16", 32, spatial, 4, g, b, wl.EPS)
+        check_groups(_decode(out, "bf16"), ref, 32 // 4 * spatial, "bf16", "stream")
