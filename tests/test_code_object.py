@@ -28,13 +28,14 @@ pytestmark = pytest.mark.skipif(
     reason="ROCm LLVM tools or the built library not available")
 
 
-def _kernels(tmp_path):
+def _code_objects(tmp_path):
+    """Paths of the library's gfx950 code objects, one per HIP source file."""
     fat = os.path.join(tmp_path, "fat.bin")
     subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section",
                     ".hip_fatbin=" + fat, binding.LIB_PATH], check=True)
     data = open(fat, "rb").read()
     starts = [m.start() for m in re.finditer(re.escape(MAGIC), data)] + [len(data)]
-    kernels = []
+    paths = []
     for n, (a, b) in enumerate(zip(starts, starts[1:])):
         part = os.path.join(tmp_path, "bundle%d" % n)
         with open(part, "wb") as f:
@@ -42,6 +43,13 @@ def _kernels(tmp_path):
         co = os.path.join(tmp_path, "co%d.o" % n)
         subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
                         "--targets=" + TARGET, "--input=" + part, "--output=" + co], check=True)
+        paths.append(co)
+    return paths
+
+
+def _kernels(tmp_path):
+    kernels = []
+    for co in _code_objects(tmp_path):
         notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", co], check=True,
                                capture_output=True, text=True).stdout
         doc = notes[notes.index("---"):]
