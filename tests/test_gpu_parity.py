@@ -222,16 +222,17 @@ def _sample_windows(T, rng, n=12, width=48):
     return wins
 
 
-def _check_sampled(out, qkv, H, D, qg, kg, cos, sin, style, seed, what):
+def _check_sampled(out, qkv, H, D, qg, kg, cos, sin, style, seed, what, x_dtype="bf16"):
     T = qkv.shape[0]
     rng = np.random.default_rng(seed)
     got_all = out.view(T, 3, H, D)
     worst = 0.0
     for a, b in _sample_windows(T, rng):
-        q_ref, k_ref = oracle_fused(qkv, "bf16", H, D, qg, kg, cos, sin, style, t_begin=a, t_end=b)
-        got = _decode(got_all[a:b].contiguous(), "bf16").reshape(b - a, 3, H, D)
-        worst = max(worst, check_close(got[:, 0], q_ref, "bf16", "%s Q[%d:%d]" % (what, a, b)),
-                    check_close(got[:, 1], k_ref, "bf16", "%s K[%d:%d]" % (what, a, b)))
+        q_ref, k_ref = oracle_fused(qkv, x_dtype, H, D, qg, kg, cos, sin, style, t_begin=a,
+                                    t_end=b)
+        got = _decode(got_all[a:b].contiguous(), x_dtype).reshape(b - a, 3, H, D)
+        worst = max(worst, check_close(got[:, 0], q_ref, x_dtype, "%s Q[%d:%d]" % (what, a, b)),
+                    check_close(got[:, 1], k_ref, x_dtype, "%s K[%d:%d]" % (what, a, b)))
     return worst
 
 
@@ -246,6 +247,24 @@ def test_headline_workload_sampled():
     assert_v_untouched(out, qkv, H, D)
     m = _check_sampled(out, qkv, H, D, qg, kg, cos, sin, "interleaved", 99, "headline")
     print("headline sampled max_abs", m)
+
+
+@pytest.mark.parametrize("x_dtype,style,table", [("fp16", "interleaved", "fp32"),
+                                                 ("bf16", "rotate_half", "bf16"),
+                                                 ("fp16", "rotate_half", "bf16")])
+def test_headline_shape_other_dtypes_and_styles(x_dtype, style, table):
+    """The headline shape and launch configuration with fp16 data, rotate-half
+    and bf16 cos/sin tables; oracle on sampled windows, V untouched."""
+    w = wl.WORKLOADS["headline"]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    qkv = wl.fused_qkv(w.seed + 7, T, H, D, x_dtype)
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, style, dtype=table)
+    out = run_fused(qkv, qg, kg, cos, sin, style)
+    assert_v_untouched(out, qkv, H, D)
+    m = _check_sampled(out, qkv, H, D, qg, kg, cos, sin, style, 98, "headline " + x_dtype,
+                       x_dtype=x_dtype)
+    print("headline", x_dtype, style, table, "sampled max_abs", m)
 
 
 @pytest.mark.slow
