@@ -11,11 +11,11 @@
 //     squared deviations) in the workspace, then gn_apply_kernel combines
 //     the group's partials with the pairwise update (sum n_i m_i / N, then
 //     sum M2_i + n_i (m_i - m)^2) in a fixed order, so every workgroup of a
-//     group gets the same statistics, re-reads its chunk and writes y.  The
-//     host runs the two kernels over slabs of groups of at most kSlabBytes
-//     (the sweep's best; the second read is mostly served from HBM, not the
-//     Infinity Cache): the stats pass reads with ordinary loads, the apply
-//     pass re-reads with non-temporal loads and writes non-temporally.
+//     group gets the same statistics, re-reads its chunk and writes y.  One
+//     launch of each covers every group (measured faster than slabs of
+//     48-192 MB, whose extra launches cost more than the Infinity Cache
+//     returns): the stats pass reads with ordinary loads, the apply pass
+//     re-reads with non-temporal loads and writes non-temporally.
 // Per vector of 8 elements (spatial is a multiple of 8, so a vector never
 // straddles channels): t = fma((x - mean) * rstd, gamma[c], beta[c]),
 // y = t * rcp(1 + exp(-t)), packed with round-to-nearest-even.
@@ -38,7 +38,6 @@ constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
 constexpr int kVpt = 8;                                   // vectors per thread per chunk
 constexpr int64_t kChunk = (int64_t)kBlock * kVpt * kVec; // 16384 elements
-constexpr int64_t kSlabBytes = 96ll << 20;                // groups per launch pair: <= 96 MB
 
 struct GnParams {
     const uint16_t* x;
@@ -46,7 +45,6 @@ struct GnParams {
     const void* gamma;
     const void* beta;
     float* partial;          // [pairs][chunks][2]: chunk mean, sum of squared deviations
-    int64_t group_begin;     // first (sample, group) pair of this launch
     int64_t group_size;      // Cg * spatial elements, a multiple of 8, < 2^31
     int32_t spatial;
     int32_t cg;
@@ -164,7 +162,7 @@ template <bool X_FP16, int PARAM>
 __global__ __launch_bounds__(kBlock) void gn_single_kernel(const GnParams p)
 {
     __shared__ float red[2][kWaves];
-    const int64_t q = p.group_begin + blockIdx.x;
+    const int64_t q = blockIdx.x;
     const int nv = chunk_vectors(p, 0);
     u32x4 v[kVpt];
     load_chunk<true>(p.x + q * p.group_size, nv, v);
@@ -179,7 +177,7 @@ template <bool X_FP16>
 __global__ __launch_bounds__(kBlock) void gn_stats_kernel(const GnParams p)
 {
     __shared__ float red[2][kWaves];
-    const int64_t q = p.group_begin + blockIdx.x / p.chunks;
+    const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
     const int nv = chunk_vectors(p, k);
     u32x4 v[kVpt];
@@ -198,7 +196,7 @@ template <bool X_FP16, int PARAM>
 __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
 {
     __shared__ float red[2][kWaves];
-    const int64_t q = p.group_begin + blockIdx.x / p.chunks;
+    const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
     const int nv = chunk_vectors(p, k);
     u32x4 v[kVpt];
@@ -325,7 +323,6 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
     p.gamma = gamma;
     p.beta = beta;
     p.partial = static_cast<float*>(workspace);
-    p.group_begin = 0;
     p.group_size = gsize;
     p.spatial = (int32_t)spatial;
     p.cg = channels / groups;
@@ -341,17 +338,6 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
 
     GnFn stats = xf ? gn_stats_kernel<true> : gn_stats_kernel<false>;
     GnFn apply = xf ? pick_apply<true>(param_dtype) : pick_apply<false>(param_dtype);
-    int64_t slab = kSlabBytes / (gsize * 2);
-    if (slab < 1)
-        slab = 1;
-    for (int64_t g0 = 0; g0 < pairs; g0 += slab) {
-        const int64_t m = pairs - g0 < slab ? pairs - g0 : slab;
-        p.group_begin = g0;
-        int r = launch(stats, m * chunks, p, s);
-        if (r == QKR_OK)
-            r = launch(apply, m * chunks, p, s);
-        if (r != QKR_OK)
-            return r;
-    }
-    return QKR_OK;
+    const int r = launch(stats, pairs * chunks, p, s);
+    return r == QKR_OK ? launch(apply, pairs * chunks, p, s) : r;
 }

@@ -109,7 +109,7 @@ def test_vae_mid_full(dtype, param_dtype):
 @pytest.mark.parametrize("key,dtype", [("gn_vae_up", "bf16"), ("gn_vae_up", "fp16"),
                                        ("gn_vae_out", "bf16")])
 def test_vae_large_sampled_groups(key, dtype):
-    """Several slabs of groups; the oracle checks first, last and a few inner groups."""
+    """Many chunks per group; the oracle checks first, last and a few inner groups."""
     w = wl.GN_WORKLOADS[key]
     x, g, b = wl.gn_inputs(w.seed, w.n, w.channels, w.spatial, dtype, "fp32")
     out = run(x, g, b, w.groups)
@@ -244,7 +244,7 @@ def test_graph_capture_replays_match_eager():
 
 def test_byte_offsets_beyond_4gib_in_place():
     """[260, 128, 256, 256] bf16 = 4.4 GB in place, 32 groups of 16 chunks:
-    8320 groups in 44 slabs; groups on both sides of the 2^32-byte offset
+    8320 groups (133,120 workgroups per pass); groups on both sides of the 2^32-byte offset
     (group 8192 starts there) against the oracle.  The samples repeat a
     4-sample block."""
     n, channels, spatial, groups, B = 260, 128, 256 * 256, 32, 4
