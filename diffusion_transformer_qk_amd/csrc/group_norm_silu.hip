@@ -2,8 +2,10 @@
 // gfx950 (the VAE step; definition in include/group_norm_silu.h).
 //
 // A group (Cg channels x spatial elements of one sample) is one contiguous
-// run of memory.  Work is cut into chunks of kChunk elements, one 256-thread
-// workgroup per (group, chunk), each thread holding kVpt 16-byte vectors:
+// run of memory.  Work is cut into chunks, one 256-thread workgroup per
+// (group, chunk), each thread holding VPT 16-byte vectors (chunks of 16384
+// elements, or 8192 / 4096 when that is needed to give a small call enough
+// workgroups):
 //   * one chunk per group: a single kernel keeps the chunk in registers,
 //     reduces mean and biased variance in two passes and writes y (one read,
 //     one write);
@@ -36,8 +38,12 @@ using qkr_host::overlaps;
 
 constexpr int kWaves = 4;
 constexpr int kBlock = kWaves * kWave;
-constexpr int kVpt = 8;                                   // vectors per thread per chunk
-constexpr int64_t kChunk = (int64_t)kBlock * kVpt * kVec; // 16384 elements
+constexpr int kVptMax = 8;                                      // vectors per thread, largest chunk
+constexpr int64_t kChunkMax = (int64_t)kBlock * kVptMax * kVec; // 16384 elements
+
+// Elements in a chunk of VPT vectors per thread.
+template <int VPT>
+constexpr int64_t chunk_elems() { return (int64_t)kBlock * VPT * kVec; }
 
 struct GnParams {
     const uint16_t* x;
@@ -54,19 +60,21 @@ struct GnParams {
 };
 
 // Vectors valid in chunk k of a group.
+template <int VPT>
 __device__ __forceinline__ int chunk_vectors(const GnParams& p, int k)
 {
+    constexpr int64_t kChunk = chunk_elems<VPT>();
     const int64_t left = p.group_size - (int64_t)k * kChunk;
     return (int)((left < kChunk ? left : kChunk) / kVec);
 }
 
 // Load the chunk's vectors; thread vectors past `nv` reload the last valid
 // vector (clamped, so every load is unconditional) and are zeroed.
-template <bool NT>
-__device__ __forceinline__ void load_chunk(const uint16_t* base, int nv, u32x4 (&v)[kVpt])
+template <bool NT, int VPT>
+__device__ __forceinline__ void load_chunk(const uint16_t* base, int nv, u32x4 (&v)[VPT])
 {
 #pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
+    for (int u = 0; u < VPT; ++u) {
         const int i = u * kBlock + threadIdx.x;
         const u32x4 t = load16<NT>(base + (int64_t)(i < nv ? i : nv - 1) * kVec);
         v[u] = i < nv ? t : u32x4{0, 0, 0, 0};
@@ -76,21 +84,22 @@ __device__ __forceinline__ void load_chunk(const uint16_t* base, int nv, u32x4 (
 // Make the compiler forget what v holds, so the fp32 values unpacked from it
 // are not kept alive (64 registers) from one pass over the chunk to the next
 // but unpacked again from the 32 packed registers.
-__device__ __forceinline__ void forget_unpacked(u32x4 (&v)[kVpt])
+template <int VPT>
+__device__ __forceinline__ void forget_unpacked(u32x4 (&v)[VPT])
 {
 #pragma unroll
-    for (int u = 0; u < kVpt; ++u)
+    for (int u = 0; u < VPT; ++u)
         __asm__ volatile("" : "+v"(v[u]));
 }
 
 // Mean and sum of squared deviations of the chunk held in v (nv valid vectors).
-template <bool X_FP16>
-__device__ __forceinline__ void chunk_moments(u32x4 (&v)[kVpt], int nv, float* red0,
+template <bool X_FP16, int VPT>
+__device__ __forceinline__ void chunk_moments(u32x4 (&v)[VPT], int nv, float* red0,
                                               float* red1, float& mean, float& m2)
 {
     float sum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
+    for (int u = 0; u < VPT; ++u) {
         float f[8];
         unpack8<X_FP16>(v[u], f);
 #pragma unroll
@@ -101,7 +110,7 @@ __device__ __forceinline__ void chunk_moments(u32x4 (&v)[kVpt], int nv, float* r
     forget_unpacked(v);
     float ss = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
+    for (int u = 0; u < VPT; ++u) {
         if (u * kBlock + (int)threadIdx.x < nv) {
             float f[8];
             unpack8<X_FP16>(v[u], f);
@@ -131,14 +140,15 @@ __device__ __forceinline__ float param(const void* table, int c)
 }
 
 // Normalise, apply the channel affine and SiLU to the chunk, store it.
-template <bool X_FP16, int PARAM>
+template <bool X_FP16, int PARAM, int VPT>
 __device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k, int nv,
-                                            const u32x4 (&v)[kVpt], float mean, float rstd)
+                                            const u32x4 (&v)[VPT], float mean, float rstd)
 {
+    constexpr int64_t kChunk = chunk_elems<VPT>();
     uint16_t* yq = p.y + q * p.group_size + (int64_t)k * kChunk;
     const int c0 = (int)(q % p.groups) * p.cg;
 #pragma unroll
-    for (int u = 0; u < kVpt; ++u) {
+    for (int u = 0; u < VPT; ++u) {
         const int i = u * kBlock + threadIdx.x;
         if (i < nv) {
             const uint32_t e = (uint32_t)(k * kChunk) + (uint32_t)i * kVec;   // < 2^31
@@ -163,8 +173,8 @@ __global__ __launch_bounds__(kBlock) void gn_single_kernel(const GnParams p)
 {
     __shared__ float red[2][kWaves];
     const int64_t q = blockIdx.x;
-    const int nv = chunk_vectors(p, 0);
-    u32x4 v[kVpt];
+    const int nv = chunk_vectors<kVptMax>(p, 0);
+    u32x4 v[kVptMax];
     load_chunk<true>(p.x + q * p.group_size, nv, v);
     float mean, m2;
     chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
@@ -173,15 +183,15 @@ __global__ __launch_bounds__(kBlock) void gn_single_kernel(const GnParams p)
 }
 
 // Several chunks, pass 1: per-chunk mean and sum of squared deviations.
-template <bool X_FP16>
+template <bool X_FP16, int VPT>
 __global__ __launch_bounds__(kBlock) void gn_stats_kernel(const GnParams p)
 {
     __shared__ float red[2][kWaves];
     const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
-    const int nv = chunk_vectors(p, k);
-    u32x4 v[kVpt];
-    load_chunk<false>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
+    const int nv = chunk_vectors<VPT>(p, k);
+    u32x4 v[VPT];
+    load_chunk<false>(p.x + q * p.group_size + (int64_t)k * chunk_elems<VPT>(), nv, v);
     float mean, m2;
     chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
     if (threadIdx.x == 0) {
@@ -192,14 +202,15 @@ __global__ __launch_bounds__(kBlock) void gn_stats_kernel(const GnParams p)
 }
 
 // Several chunks, pass 2: combine the group's partials, write the chunk.
-template <bool X_FP16, int PARAM>
+template <bool X_FP16, int PARAM, int VPT>
 __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
 {
+    constexpr int64_t kChunk = chunk_elems<VPT>();
     __shared__ float red[2][kWaves];
     const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
-    const int nv = chunk_vectors(p, k);
-    u32x4 v[kVpt];
+    const int nv = chunk_vectors<VPT>(p, k);
+    u32x4 v[VPT];
     load_chunk<true>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
 
     const float* part = p.partial + 2 * q * p.chunks;
@@ -230,11 +241,18 @@ GnFn pick_single(int prm)
          : prm == QKR_FP16 ? gn_single_kernel<XF, QKR_FP16> : gn_single_kernel<XF, QKR_BF16>;
 }
 
-template <bool XF>
+template <bool XF, int VPT>
 GnFn pick_apply(int prm)
 {
-    return prm == QKR_FP32 ? gn_apply_kernel<XF, QKR_FP32>
-         : prm == QKR_FP16 ? gn_apply_kernel<XF, QKR_FP16> : gn_apply_kernel<XF, QKR_BF16>;
+    return prm == QKR_FP32 ? gn_apply_kernel<XF, QKR_FP32, VPT>
+         : prm == QKR_FP16 ? gn_apply_kernel<XF, QKR_FP16, VPT> : gn_apply_kernel<XF, QKR_BF16, VPT>;
+}
+
+template <int VPT>
+void pick_pair(bool xf, int prm, GnFn* stats, GnFn* apply)
+{
+    *stats = xf ? gn_stats_kernel<true, VPT> : gn_stats_kernel<false, VPT>;
+    *apply = xf ? pick_apply<true, VPT>(prm) : pick_apply<false, VPT>(prm);
 }
 
 int launch(GnFn fn, int64_t blocks, const GnParams& p, hipStream_t stream)
@@ -247,9 +265,17 @@ int launch(GnFn fn, int64_t blocks, const GnParams& p, hipStream_t stream)
     return QKR_OK;
 }
 
-// Shape checks shared by the size query and the call; sets chunks and pairs.
+// Workgroups per pass below which groups are cut into smaller chunks: with
+// 16K-element chunks a small call leaves most of the chip idle (the VAE mid
+// stage, 32 groups of 262,144, runs 512 workgroups).
+constexpr int64_t kFillBlocks = 2048;
+
+// Shape checks shared by the size query and the call.  Sets pairs (samples x
+// groups), the vectors per thread of a chunk (8, 4 or 2: the largest that
+// still gives kFillBlocks workgroups, 8 for a group of one chunk) and the
+// chunks per group.
 int check_shape(int64_t n, int32_t channels, int64_t spatial, int32_t groups, int64_t* chunks,
-                int64_t* pairs)
+                int64_t* pairs, int* vpt)
 {
     if (n < 0 || channels < 1 || groups < 1 || channels % groups)
         return QKR_ERR_SHAPE;
@@ -258,15 +284,24 @@ int check_shape(int64_t n, int32_t channels, int64_t spatial, int32_t groups, in
     const int64_t gsize = (int64_t)(channels / groups) * spatial;
     if (gsize >= (1ll << 31))
         return QKR_ERR_SHAPE;
-    *chunks = (gsize + kChunk - 1) / kChunk;
     if (n > ((1ll << 31) - 1) / groups)
         return QKR_ERR_SHAPE;
     *pairs = n * groups;
+    *vpt = kVptMax;
+    if (gsize > kChunkMax) {
+        for (int v = kVptMax; v >= 2; v /= 2) {
+            *vpt = v;
+            const int64_t elems = (int64_t)kBlock * v * kVec;
+            if (*pairs * ((gsize + elems - 1) / elems) >= kFillBlocks)
+                break;
+        }
+    }
+    const int64_t elems = (int64_t)kBlock * *vpt * kVec;
+    *chunks = (gsize + elems - 1) / elems;
     if (*pairs * *chunks >= (1ll << 31))
         return QKR_ERR_SHAPE;
     return QKR_OK;
 }
-
 
 }  // namespace
 
@@ -274,7 +309,8 @@ extern "C" int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channel
                                                       int32_t groups)
 {
     int64_t chunks = 0, pairs = 0;
-    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs);
+    int vpt = 0;
+    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs, &vpt);
     if (rc != QKR_OK)
         return rc;
     return chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
@@ -292,7 +328,8 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
     if (!(eps > 0.0f) || !isfinite(eps))
         return QKR_ERR_ARG;
     int64_t chunks = 0, pairs = 0;
-    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs);
+    int vpt = 0;
+    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs, &vpt);
     if (rc != QKR_OK)
         return rc;
     if (n == 0)
@@ -336,8 +373,13 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
         return launch(xf ? pick_single<true>(param_dtype) : pick_single<false>(param_dtype), pairs,
                       p, s);
 
-    GnFn stats = xf ? gn_stats_kernel<true> : gn_stats_kernel<false>;
-    GnFn apply = xf ? pick_apply<true>(param_dtype) : pick_apply<false>(param_dtype);
+    GnFn stats, apply;
+    if (vpt == 8)
+        pick_pair<8>(xf, param_dtype, &stats, &apply);
+    else if (vpt == 4)
+        pick_pair<4>(xf, param_dtype, &stats, &apply);
+    else
+        pick_pair<2>(xf, param_dtype, &stats, &apply);
     const int r = launch(stats, pairs * chunks, p, s);
     return r == QKR_OK ? launch(apply, pairs * chunks, p, s) : r;
 }

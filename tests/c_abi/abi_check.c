@@ -62,7 +62,7 @@ int main(void)
            QKR_ERR_SHAPE);
     EXPECT(dit_fuse_scale_shift(a, b, 4, 6144, 1, NULL, a, QKR_FP32, 1e-6f, QKR_BF16, NULL),
            QKR_ERR_NULL);
-    if (dit_group_norm_silu_workspace_size(1, 512, 128 * 128, 32) != 32 * 16 * 8) {
+    if (dit_group_norm_silu_workspace_size(1, 512, 128 * 128, 32) != 32 * 64 * 8) {
         printf("FAIL workspace size\n");
         return 1;
     }

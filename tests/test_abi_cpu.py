@@ -210,11 +210,15 @@ def gn(**over):
 
 
 def test_group_norm_workspace_size():
+    """8 bytes per chunk; chunks of 16384 elements, or 8192 / 4096 when a call
+    would otherwise run fewer than 2048 workgroups; nothing for one chunk."""
     ws = qkr.group_norm_silu_workspace_size
-    assert ws(1, 512, 128 * 128, 32) == 32 * 16 * 8          # 16 chunks of 16384 per group
-    assert ws(1, 128, 1024 * 1024, 32) == 32 * 256 * 8
+    assert ws(1, 128, 1024 * 1024, 32) == 32 * 256 * 8      # 8192 workgroups of 16384
+    assert ws(1, 512, 128 * 128, 32) == 32 * 64 * 8         # 512 or 1024 would be too few: 4096
+    assert ws(4, 256, 30000, 32) == 128 * 30 * 8            # 1920 at 16384, 3840 at 8192
+    assert ws(4, 512, 16392, 32) == 128 * 17 * 8            # 2176 at 16384 (ragged)
     assert ws(2, 64, 4096, 32) == 0                         # 8192-element groups: one chunk
-    assert ws(1, 6, 16384 * 2 + 8, 2) == 2 * 7 * 8          # 3*(32776) -> 7 chunks
+    assert ws(1, 6, 16384 * 2 + 8, 2) == 2 * 25 * 8         # 98328 elements in 4096s
     assert ws(1, 64, 12, 32) == b.QKR_ERR_UNSUPPORTED       # spatial not a multiple of 8
     assert ws(1, 60, 64, 32) == b.QKR_ERR_SHAPE             # groups do not divide channels
     assert ws(-1, 64, 64, 32) == b.QKR_ERR_SHAPE

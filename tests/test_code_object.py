@@ -82,9 +82,9 @@ def test_every_source_file_contributes_its_kernels(kernels):
     # 8 row lengths x 2 data dtypes x 3 modulation dtypes x {1, 4} rows per
     # workgroup x {rows of exactly 512 * vectors per lane, other rows}
     assert fams.get("fuse_scale_shift_kernel") == 192, fams
-    for fam in ("gn_single_kernel", "gn_apply_kernel"):
-        assert fams.get(fam) == 6, fams          # 2 data dtypes x 3 affine dtypes
-    assert fams.get("gn_stats_kernel") == 2, fams
+    assert fams.get("gn_single_kernel") == 6, fams   # 2 data dtypes x 3 affine dtypes
+    assert fams.get("gn_apply_kernel") == 18, fams   # ... x 3 chunk sizes
+    assert fams.get("gn_stats_kernel") == 6, fams    # 2 data dtypes x 3 chunk sizes
 
 
 def test_no_kernel_uses_scratch_or_spills(kernels):

@@ -176,9 +176,9 @@ def test_constant_groups_and_zero_gamma():
 def test_workspace_errors_and_explicit_workspace():
     n, channels, spatial, groups = 1, 64, 64 * 64, 32     # 8192-element groups: no workspace
     assert qkr.group_norm_silu_workspace_size(n, channels, spatial, groups) == 0
-    n, channels, spatial, groups = 1, 32, 128 * 128, 8    # 65536-element groups: 4 chunks
+    n, channels, spatial, groups = 1, 32, 128 * 128, 8    # 65536-element groups: 16 chunks
     need = qkr.group_norm_silu_workspace_size(n, channels, spatial, groups)
-    assert need == 8 * 4 * 8
+    assert need == 8 * 16 * 8
     x, g, b = wl.gn_inputs(10, n, channels, spatial, "bf16", "fp32")
     xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
     short = torch.empty(need - 8, dtype=torch.uint8, device=DEV)
@@ -280,3 +280,22 @@ def test_concurrent_streams_are_independent():
     for (x, g, b, spatial, *_), out in zip(cases, outs):
         ref = oracle_groups(x, "bf16", 32, spatial, 4, g, b, wl.EPS)
         check_groups(_decode(out, "bf16"), ref, 32 // 4 * spatial, "bf16", "stream")
+
+
+@pytest.mark.parametrize("n,channels,spatial,chunk", [
+    (4, 512, 16392, 16384),     # 2176 workgroups at 16384: a 128-element last chunk
+    (4, 256, 30000, 8192),      # 1920 at 16384, so 8192: a 2432-element last chunk
+    (1, 512, 128 * 128, 4096),  # the VAE mid stage: 4096-element chunks
+])
+def test_chunk_size_follows_call_size(n, channels, spatial, chunk):
+    groups = 32
+    gsize = channels // groups * spatial
+    chunks = -(-gsize // chunk)
+    assert qkr.group_norm_silu_workspace_size(n, channels, spatial, groups) == n * groups * chunks * 8
+    x, g, b = wl.gn_inputs(n * 31 + spatial, n, channels, spatial, "bf16", "fp32")
+    out = run(x, g, b, groups)
+    flat = out.reshape(-1)
+    for q in sorted({0, 1, n * groups // 2, n * groups - 1}):
+        ref = oracle_groups(x, "bf16", channels, spatial, groups, g, b, wl.EPS, q, q + 1)
+        check_groups(_decode(flat[q * gsize:(q + 1) * gsize], "bf16"), ref, gsize, "bf16",
+                     "chunk %d group %d" % (chunk, q))
