@@ -5,8 +5,10 @@ of every token), in place on a device-resident fused QKV buffer.  Default
 workload: Wan-A14B-shaped 32760 tokens x 3*40*128 bf16, interleaved RoPE,
 one shared fp32 cos/sin row per token.
 
-Prints ONE JSON line.  ``value`` is achieved algorithmic HBM throughput over
-the K timed steps (GB/s, bytes the pass must move / time);
+Prints ONE JSON line.  ``dtype`` is the arithmetic type of the kernels (fp32:
+16-bit data are widened exactly, computed in fp32 and rounded once);
+``config.data_dtype`` is the storage type.  ``value`` is achieved algorithmic
+HBM throughput over the K timed steps (GB/s, bytes the pass must move / time);
 ``roofline.achieved`` uses the mean kernel duration from HIP events recorded
 around each launch on the launch stream; ``cpu_baseline`` times the fp64 CPU
 oracle on a bounded sample of the same workload.
@@ -337,13 +339,13 @@ def bench_fuse_scale_shift(args):
         "metric": "AdaLN fuse_scale_shift µs/call and achieved HBM GB/s (% of peak)",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(region_ms / K, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: x %s [%d, %d], %d modulation row(s) %s%s%s"
                                % (w.key, dtype, w.rows, w.hidden, w.batches, args.mod_dtype,
                                   ", in place" if args.inplace else "",
                                   ", cache flushed" if args.flush else ""),
-                   "rows": w.rows, "hidden": w.hidden, "batches": w.batches, "math": "f32",
+                   "rows": w.rows, "hidden": w.hidden, "batches": w.batches, "data_dtype": dtype,
                    "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
                         "p10": round(float(np.percentile(per, 10)), 2),
@@ -398,14 +400,14 @@ def bench_group_norm_silu(args):
         "metric": "group_norm_silu µs/call and achieved HBM GB/s (% of peak)",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(region_ms / K, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: x %s [%d, %d, %d, %d], %d groups, %s affine%s%s"
                                % (w.key, dtype, w.n, w.channels, w.height, w.width, w.groups,
                                   args.mod_dtype, ", in place" if args.inplace else "",
                                   ", cache flushed" if args.flush else ""),
                    "n": w.n, "channels": w.channels, "spatial": w.spatial, "groups": w.groups,
-                   "workspace_bytes": need, "math": "f32", "parallelism": "single GPU"},
+                   "workspace_bytes": need, "data_dtype": dtype, "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
                         "p10": round(float(np.percentile(per, 10)), 2),
                         "p90": round(float(np.percentile(per, 90)), 2)},
@@ -530,7 +532,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %s %s [%d, %s%dx%d], %s RoPE, %s %s cos/sin%s"
                                % (w.key, "fused QKV" if w.layout == "fused" else "separate q, k",
@@ -538,7 +540,7 @@ def main():
                                   args.layout, args.cos_dtype,
                                   ", cache flushed" if args.flush else ""),
                    "tokens": T, "heads": H, "head_dim": D, "layout": args.layout,
-                   "style": style, "math": "f32", "parallelism": "single GPU"},
+                   "style": style, "data_dtype": dtype, "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
                         "p10": round(float(np.percentile(per, 10)), 2),
                         "p90": round(float(np.percentile(per, 90)), 2)},
