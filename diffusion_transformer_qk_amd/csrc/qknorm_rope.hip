@@ -311,7 +311,7 @@ __global__ __launch_bounds__(WAVES * kWave) void qknorm_rope_kernel(const Params
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWavesPerBlock * kWave;
 constexpr int kNonTemporal = 3;         // Q/K loads and stores are not retained in cache
-constexpr int kUnrollPerHead = 4;       // per-head layout also keeps 2 table rows per head
+constexpr int kUnrollPerHeadMax = 10;   // per-head layout also keeps 2 table rows per head
 constexpr int kDieRunsFromBlocks = 4096;
 
 // ---------------------------------------------------------------- dispatch
@@ -319,7 +319,9 @@ constexpr int kDieRunsFromBlocks = 4096;
 // Scheduling only (every choice computes bit-identical output):
 //   unroll  the smallest of {3, 6, 10, 12} head iterations covering all H
 //           heads (capped at 12), so a wave keeps one slice's loads in flight
-//           with few padded iterations; the per-head layout uses 4;
+//           with few padded iterations; the per-head layout, whose table rows
+//           take registers too, caps it at 10 (measured on 40 heads: 4 / 8 /
+//           10 iterations in flight gave 490 / 479 / 473 us);
 //   order   one contiguous run of tokens per die when one buffer is streamed
 //           (fused QKV or a single tensor) and the grid has at least
 //           kDieRunsFromBlocks workgroups; hardware order otherwise (two
@@ -340,7 +342,9 @@ Launch plan_launch(int head_dim, int heads, int64_t tokens, int n_tensors, bool 
     Launch l;
     const int heads_per_iter = kWave / (head_dim / kVec);
     const int iters = (heads + heads_per_iter - 1) / heads_per_iter;
-    l.unroll = per_head ? kUnrollPerHead : iters <= 3 ? 3 : iters <= 6 ? 6 : iters <= 10 ? 10 : 12;
+    l.unroll = iters <= 3 ? 3 : iters <= 6 ? 6 : iters <= 10 ? 10 : 12;
+    if (per_head && l.unroll > kUnrollPerHeadMax)
+        l.unroll = kUnrollPerHeadMax;
     l.tokens_per_block = kWavesPerBlock / n_tensors;
     l.blocks = (tokens + l.tokens_per_block - 1) / l.tokens_per_block;
     l.order = (!separate_pair && l.blocks >= kDieRunsFromBlocks) ? -1 : 0;
@@ -351,7 +355,11 @@ template <int D, int STYLE, bool PH, bool CB, bool XF, int ORDER>
 KernelFn kernel_for_unroll(int unroll)
 {
     if constexpr (PH) {
-        return qknorm_rope_kernel<D, STYLE, PH, CB, XF, kUnrollPerHead, kWavesPerBlock,
+        if (unroll == 3)
+            return qknorm_rope_kernel<D, STYLE, PH, CB, XF, 3, kWavesPerBlock, kNonTemporal, ORDER>;
+        if (unroll == 6)
+            return qknorm_rope_kernel<D, STYLE, PH, CB, XF, 6, kWavesPerBlock, kNonTemporal, ORDER>;
+        return qknorm_rope_kernel<D, STYLE, PH, CB, XF, kUnrollPerHeadMax, kWavesPerBlock,
                                   kNonTemporal, ORDER>;
     } else {
         if (unroll == 3)

@@ -76,9 +76,9 @@ def test_every_source_file_contributes_its_kernels(kernels):
     fams = {}
     for k in kernels:
         fams[_family(k[".name"])] = fams.get(_family(k[".name"]), 0) + 1
-    # 2 head dims x 2 styles x 2 layouts x 2 table dtypes x 2 data dtypes x
-    # 5 (unroll, block order) pairs
-    assert fams.get("qknorm_rope_kernel") == 160, fams
+    # 2 head dims x 2 styles x 2 table dtypes x 2 data dtypes x 2 block orders x
+    # (4 unroll depths, shared layout + 3, per-head layout)
+    assert fams.get("qknorm_rope_kernel") == 224, fams
     # 8 row lengths x 2 data dtypes x 3 modulation dtypes x {1, 4} rows per
     # workgroup x {rows of exactly 512 * vectors per lane, other rows}
     assert fams.get("fuse_scale_shift_kernel") == 192, fams

@@ -158,11 +158,13 @@ def test_kernels_do_not_spill(head_dim, layout):
                         info = qkr.kernel_info(head_dim, layout, cd, style, xd, heads=heads,
                                                tokens=tokens)
                         assert info["scratch_bytes"] == 0, info
-                        assert 0 < info["num_vgprs"] <= 128, info
+                        # the per-head layout also holds each head's table rows:
+                        # up to 10 heads' worth in flight, 2 waves per SIMD
+                        limit = 256 if layout == "per_head" else 128
+                        assert 0 < info["num_vgprs"] <= limit, info
                         seen.add((info["heads_in_flight"], info["die_runs"]))
-    want = ({(4, 0), (4, 1)} if layout == "per_head" else
-            {(u, o) for u in (3, 6, 10, 12) for o in (0, 1)})
-    assert want <= seen, seen
+    depths = (3, 6, 10) if layout == "per_head" else (3, 6, 10, 12)
+    assert {(u, o) for u in depths for o in (0, 1)} <= seen, seen
 
 
 # ----------------------------------------------------------------------------- the five workloads
