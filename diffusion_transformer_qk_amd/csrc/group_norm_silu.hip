@@ -269,6 +269,8 @@ int launch(GnFn fn, int64_t blocks, const GnParams& p, hipStream_t stream)
 // 16K-element chunks a small call leaves most of the chip idle (the VAE mid
 // stage, 32 groups of 262,144, runs 512 workgroups).
 constexpr int64_t kFillBlocks = 2048;
+// A launch grid holds fewer than 2^32 work-items.
+constexpr int64_t kMaxBlocks = 0xFFFFFFFFll / kBlock;
 
 // Shape checks shared by the size query and the call.  Sets pairs (samples x
 // groups), the vectors per thread of a chunk (8, 4 or 2: the largest that
@@ -298,7 +300,7 @@ int check_shape(int64_t n, int32_t channels, int64_t spatial, int32_t groups, in
     }
     const int64_t elems = (int64_t)kBlock * *vpt * kVec;
     *chunks = (gsize + elems - 1) / elems;
-    if (*pairs * *chunks >= (1ll << 31))
+    if (*pairs * *chunks > kMaxBlocks)
         return QKR_ERR_SHAPE;
     return QKR_OK;
 }

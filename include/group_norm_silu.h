@@ -50,6 +50,11 @@ int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channels, int64_t 
  * n                >= 0 (0 is a no-op returning QKR_OK once scalars are valid).
  * channels, groups >= 1, groups divides channels.
  * spatial          >= 8, a multiple of 8; channels/groups * spatial < 2^31.
+ *                  The call takes one 256-thread workgroup per chunk of a
+ *                  group (up to 16,384 elements; one chunk for a group that
+ *                  fits); more than 2^24 - 1 workgroups (a launch grid holds
+ *                  fewer than 2^32 work-items) is QKR_ERR_SHAPE, which in
+ *                  practice only n * groups >= 2^24 small groups reach.
  * gamma, beta      [channels] of param_dtype (QKR_BF16, QKR_FP16, QKR_FP32).
  * eps              finite and > 0, added to the variance inside the root.
  * dtype            QKR_BF16 or QKR_FP16 (x and y).

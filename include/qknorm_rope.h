@@ -56,8 +56,11 @@ enum { QKR_COS_SHARED = 0, QKR_COS_PER_HEAD = 1 };
 /* RoPE pairing styles. */
 enum { QKR_ROPE_INTERLEAVED = 0, QKR_ROPE_ROTATE_HALF = 1 };
 
-/* Limits checked by qknorm_rope_fused. */
-#define QKR_MAX_TOKENS ((int64_t)1 << 31)   /* tokens must be below this     */
+/* Limits checked by qknorm_rope_fused (and, for rows, dit_fuse_scale_shift).
+ * A launch grid holds fewer than 2^32 work-items; with 256-thread workgroups
+ * of two tokens (one row for short AdaLN calls: 64 threads) 2^24 tokens stay
+ * far inside it. */
+#define QKR_MAX_TOKENS ((int64_t)1 << 24)   /* tokens must be below this     */
 #define QKR_MAX_HEADS 65536                 /* heads must not exceed this    */
 
 /*

@@ -67,6 +67,7 @@ def call(**over):
     (dict(eps=float("nan")), b.QKR_ERR_ARG),
     (dict(eps=float("inf")), b.QKR_ERR_ARG),
     (dict(tokens=-1), b.QKR_ERR_SHAPE),
+    (dict(tokens=1 << 24), b.QKR_ERR_SHAPE),       # grid limit: 2^23 workgroups of 256
     (dict(tokens=1 << 31), b.QKR_ERR_SHAPE),
     (dict(heads=0), b.QKR_ERR_SHAPE),
     (dict(heads=65537), b.QKR_ERR_SHAPE),
@@ -161,6 +162,7 @@ def fss(**over):
     (dict(eps=0.0), b.QKR_ERR_ARG),
     (dict(eps=float("nan")), b.QKR_ERR_ARG),
     (dict(rows=-2), b.QKR_ERR_SHAPE),
+    (dict(rows=1 << 24), b.QKR_ERR_SHAPE),
     (dict(rows=1 << 31), b.QKR_ERR_SHAPE),
     (dict(rows_per_batch=0), b.QKR_ERR_SHAPE),
     (dict(x=0), b.QKR_ERR_NULL),
@@ -223,6 +225,10 @@ def test_group_norm_workspace_size():
     assert ws(1, 60, 64, 32) == b.QKR_ERR_SHAPE             # groups do not divide channels
     assert ws(-1, 64, 64, 32) == b.QKR_ERR_SHAPE
     assert ws(1, 2, 1 << 31, 1) == b.QKR_ERR_UNSUPPORTED
+    # one workgroup per chunk, and a grid holds fewer than 2^32 work-items of 256
+    assert ws((1 << 24) - 1, 1, 8, 1) == 0                  # 2^24 - 1 one-chunk groups
+    assert ws(1 << 22, 4, 8, 4) == b.QKR_ERR_SHAPE          # 2^24 one-chunk groups
+    assert ws(1 << 10, 16, 16384 * 1024, 16) == b.QKR_ERR_SHAPE   # 2^14 pairs x 1024 chunks
 
 
 @pytest.mark.parametrize("over,code", [
