@@ -196,6 +196,9 @@ def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
             raise ValueError("q/k must be [..., heads, head_dim]")
         head_dim = ref.shape[-1] if head_dim is None else head_dim
         heads = ref.shape[-2] if heads is None else heads
+        if tuple(ref.shape[-2:]) != (heads, head_dim):
+            raise ValueError("q/k must be [..., heads, head_dim] = [..., %d, %d]"
+                             % (heads, head_dim))
         tokens = ref.numel() // (heads * head_dim) if ref.numel() else 0
         if q is not None and k is not None and (q.shape != k.shape or q.dtype != k.dtype):
             raise ValueError("q and k must have the same shape and dtype")

@@ -140,6 +140,11 @@ def test_python_binding_rejects_cpu_tensors():
         qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c)
     with pytest.raises(ValueError):   # wrong table size
         qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c[:3], sin=c[:3])
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="heads, head_dim"):   # heads disagree with the shape
+        qkr.qknorm_rope_fused(q=q, q_gamma=g, cos=c, sin=c, heads=4)
+    with pytest.raises(ValueError, match="heads, head_dim"):
+        qkr.qknorm_rope_fused(q=q.view(4, 128), q_gamma=g, cos=c, sin=c, heads=2, head_dim=64)
 
 
 # ----------------------------------------------------------------------------- AdaLN entry point
