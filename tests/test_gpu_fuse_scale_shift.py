@@ -290,3 +290,31 @@ def test_concurrent_streams_are_independent():
         y, n = oracle_rows(x, "fp16", sc, sh, rows, wl.EPS, rows - 64, rows)
         check_rows(_decode(out[rows - 64:], "fp16"), y, n, sc, sh, rows, rows - 64, "fp16",
                    "stream tail")
+
+
+def test_maximum_rows():
+    """The largest row count the library takes: rows = 2^24 - 1 of hidden 8
+    (268 MB), three batches of 5,592,405 rows, 2^22 staging workgroups.
+    Sampled rows at both ends, the middle and every batch boundary against the
+    oracle.  Rows repeat a 4096-row block (the step is per row)."""
+    rows, hidden, B, batches = (1 << 24) - 1, 8, 4096, 3
+    rpb = rows // batches
+    block, sc, sh = wl.adaln_inputs(4747, B, hidden, batches, "bf16", "fp32")
+    blk = block.to(DEV)
+    n = rows // B
+    x = torch.empty((rows, hidden), dtype=torch.bfloat16, device=DEV)
+    x[:n * B].view(n, B, hidden).copy_(blk.unsqueeze(0).expand(n, -1, -1))
+    x[n * B:].copy_(blk[:rows - n * B])
+    y = qkr.fuse_scale_shift(x, sc.to(DEV), sh.to(DEV), rows_per_batch=rpb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4748)
+    samples = sorted({0, 1, B, rpb - 1, rpb, 2 * rpb - 1, 2 * rpb, rows // 2, rows - 2,
+                      rows - 1, *rng.integers(0, rows, 20).tolist()})
+    got_all = _decode(y[torch.tensor(samples, device=DEV)], "bf16")
+    m = 0.0
+    for i, r in enumerate(samples):
+        b = r // rpb
+        yr, nr = oracle_rows(block[r % B:r % B + 1], "bf16", sc[b:b + 1], sh[b:b + 1], 1, wl.EPS)
+        m = max(m, check_rows(got_all[i:i + 1], yr, nr, sc[b:b + 1], sh[b:b + 1], 1, 0, "bf16",
+                              "row %d" % r))
+    print("maximum rows max_abs", m)

@@ -299,3 +299,31 @@ def test_chunk_size_follows_call_size(n, channels, spatial, chunk):
         ref = oracle_groups(x, "bf16", channels, spatial, groups, g, b, wl.EPS, q, q + 1)
         check_groups(_decode(flat[q * gsize:(q + 1) * gsize], "bf16"), ref, gsize, "bf16",
                      "chunk %d group %d" % (chunk, q))
+
+
+def test_maximum_workgroups():
+    """The largest grid the library launches: n = 2^24 - 1 samples of one
+    8-element group ([16777215, 1, 8] bf16, 268 MB), one single-read workgroup
+    each, 2^24 - 1 workgroups of 256 threads (the most a launch grid holds).
+    Sampled groups at both ends and the middle against the oracle.  Samples
+    repeat a 4096-sample block (the step is per group)."""
+    n, channels, spatial, groups, B = (1 << 24) - 1, 1, 8, 1, 4096
+    assert qkr.group_norm_silu_workspace_size(n, channels, spatial, groups) == 0
+    block, g, b = wl.gn_inputs(4949, B, channels, spatial, "bf16", "fp32")
+    blk = block.to(DEV).view(B, -1)
+    k = n // B
+    x = torch.empty((n, channels, spatial), dtype=torch.bfloat16, device=DEV)
+    flat = x.view(n, -1)
+    flat[:k * B].view(k, B, -1).copy_(blk.unsqueeze(0).expand(k, -1, -1))
+    flat[k * B:].copy_(blk[:n - k * B])
+    y = qkr.group_norm_silu(x, g.to(DEV), b.to(DEV), groups)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4950)
+    samples = sorted({0, 1, B - 1, B, n // 2, n - 2, n - 1, *rng.integers(0, n, 20).tolist()})
+    got_all = _decode(y.view(n, -1)[torch.tensor(samples, device=DEV)], "bf16")
+    m = 0.0
+    for i, q in enumerate(samples):
+        ref = oracle_groups(block, "bf16", channels, spatial, groups, g, b, wl.EPS,
+                            q % B, q % B + 1)
+        m = max(m, check_groups(got_all[i], ref, spatial, "bf16", "group %d" % q))
+    print("maximum workgroups max_abs", m)

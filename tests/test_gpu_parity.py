@@ -569,3 +569,50 @@ def test_concurrent_streams_are_independent():
     torch.cuda.synchronize()
     for qkv, qg, kg, cos, sin, style, x, *_ in cases:
         compare_fused(x.cpu(), qkv, "fp16", H, D, qg, kg, cos, sin, style, what="streams")
+
+
+def _repeat_rows(block_dev: torch.Tensor, total: int) -> torch.Tensor:
+    """[total, width] device tensor repeating the rows of block_dev."""
+    b = block_dev.shape[0]
+    out = torch.empty((total, block_dev.shape[1]), dtype=block_dev.dtype, device=DEV)
+    n = total // b
+    out[:n * b].view(n, b, -1).copy_(block_dev.unsqueeze(0).expand(n, -1, -1))
+    out[n * b:].copy_(block_dev[:total - n * b])
+    return out
+
+
+def test_maximum_tokens():
+    """The largest call the library takes: tokens = 2^24 - 1, one 64-wide head,
+    fused [16777215, 3*64] bf16 (6.4 GB) with 4.3 GB fp32 cos and sin tables,
+    a grid of 2^23 workgroups in per-die runs.  Sampled tokens from both ends
+    and the middle against the oracle; V untouched everywhere.  Activations and
+    table rows repeat a 4096-token block (the pass is per token)."""
+    T, H, D, B = (1 << 24) - 1, 1, 64, 4096
+    block = wl.fused_qkv(4545, B, H, D, "bf16")
+    qg, kg = wl.norm_weights(4545, D)
+    cos, sin = tables(np.arange(B) * 7, (D // 2,), D, "interleaved")
+    blk = block.to(DEV)
+    x = _repeat_rows(blk, T)
+    c, s = _repeat_rows(dev(cos), T), _repeat_rows(dev(sin), T)
+    info = qkr.kernel_info(D, "shared", qkr.binding.QKR_FP32, "interleaved",
+                           qkr.binding.QKR_BF16, heads=H, tokens=T)
+    assert info["die_runs"] == 1 and info["tokens_per_block"] == 2
+    qkr.qknorm_rope_fused(x, q_gamma=dev(qg), k_gamma=dev(kg), cos=c, sin=s, style="interleaved")
+    torch.cuda.synchronize()
+    del c, s
+    n = T // B
+    xb, bb = x.view(torch.int16), blk.view(torch.int16)
+    v = xb[:n * B].view(n, B, -1)[:, :, 2 * H * D:]
+    assert torch.equal(v, bb[:, 2 * H * D:].unsqueeze(0).expand(n, -1, -1)), "V changed"
+    assert torch.equal(xb[n * B:, 2 * H * D:], bb[:T - n * B, 2 * H * D:]), "V changed"
+    rng = np.random.default_rng(4546)
+    samples = sorted({0, 1, B - 1, B, T // 2, T - B, T - 2, T - 1,
+                      *rng.integers(0, T, 24).tolist()})
+    idx = torch.tensor(samples)
+    rows = block[idx % B]
+    q_ref, k_ref = oracle_fused(rows, "bf16", H, D, qg, kg, cos[idx % B], sin[idx % B],
+                                "interleaved")
+    got = _decode(x[idx.to(DEV)], "bf16").reshape(len(samples), 3, H, D)
+    m = max(check_close(got[:, 0], q_ref, "bf16", "max tokens Q"),
+            check_close(got[:, 1], k_ref, "bf16", "max tokens K"))
+    print("maximum tokens max_abs", m)
