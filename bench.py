@@ -96,7 +96,7 @@ def parse():
                     choices=["qknorm_rope", "fuse_scale_shift", "group_norm_silu"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mod-dtype", default="fp32", choices=["fp32", "bf16", "fp16"])
-    ap.add_argument("--inplace", action="store_true", help="AdaLN: write y over x")
+    ap.add_argument("--inplace", action="store_true", help="AdaLN, group norm: write y over x")
     ap.add_argument("--layout", default="shared", choices=["shared", "per_head"])
     ap.add_argument("--style", default=None, choices=[None, "interleaved", "rotate_half"])
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])

@@ -19,7 +19,7 @@
 //     returns): the stats pass reads with ordinary loads, the apply pass
 //     re-reads with non-temporal loads and writes non-temporally.
 // Per vector of 8 elements (spatial is a multiple of 8, so a vector never
-// straddles channels): t = fma((x - mean) * rstd, gamma[c], beta[c]),
+// straddles channels): t = fma(x - mean, rstd * gamma[c], beta[c]),
 // y = t * rcp(1 + exp(-t)), packed with round-to-nearest-even.
 #include <hip/hip_runtime.h>
 
@@ -139,7 +139,13 @@ __device__ __forceinline__ float param(const void* table, int c)
     }
 }
 
-// Normalise, apply the channel affine and SiLU to the chunk, store it.
+// Normalise, apply the channel affine and SiLU to the chunk, store it:
+// t = fma(x - mean, a[c], beta[c]) with a[c] = rstd * gamma[c] formed once
+// per channel, then y = t * rcp(1 + exp(-t)).  When a channel holds at least
+// a chunk, the chunk covers at most two channels: their coefficients come from
+// uniform addresses once, and each vector picks one by comparing its offset
+// with the channel boundary.  Otherwise each vector divides its offset by
+// spatial to find its channel.
 template <bool X_FP16, int PARAM, int VPT>
 __device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k, int nv,
                                             const u32x4 (&v)[VPT], float mean, float rstd)
@@ -147,19 +153,41 @@ __device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k,
     constexpr int64_t kChunk = chunk_elems<VPT>();
     uint16_t* yq = p.y + q * p.group_size + (int64_t)k * kChunk;
     const int c0 = (int)(q % p.groups) * p.cg;
+    const uint32_t e0 = (uint32_t)(k * kChunk);           // chunk offset in the group, < 2^31
+    const uint32_t sp = (uint32_t)p.spatial;
+    const bool two = sp >= (uint32_t)kChunk;
+    float a0 = 0.0f, b0 = 0.0f, a1 = 0.0f, b1 = 0.0f;
+    uint32_t boundary = 0;
+    if (two) {
+        const uint32_t ci = e0 / sp;                       // the chunk's first channel in the group
+        boundary = (ci + 1) * sp;                          // where the next channel starts (<= group size)
+        const int c = c0 + (int)ci;
+        const int cn = ci + 1 < (uint32_t)p.cg ? c + 1 : c;
+        a0 = rstd * param<PARAM>(p.gamma, c);
+        b0 = param<PARAM>(p.beta, c);
+        a1 = rstd * param<PARAM>(p.gamma, cn);
+        b1 = param<PARAM>(p.beta, cn);
+    }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
         const int i = u * kBlock + threadIdx.x;
         if (i < nv) {
-            const uint32_t e = (uint32_t)(k * kChunk) + (uint32_t)i * kVec;   // < 2^31
-            const int c = c0 + (int)(e / (uint32_t)p.spatial);
-            const float g = param<PARAM>(p.gamma, c);
-            const float b = param<PARAM>(p.beta, c);
+            const uint32_t e = e0 + (uint32_t)i * kVec;
+            float a, b;
+            if (two) {
+                const bool next = e >= boundary;
+                a = next ? a1 : a0;
+                b = next ? b1 : b0;
+            } else {
+                const int c = c0 + (int)(e / sp);
+                a = rstd * param<PARAM>(p.gamma, c);
+                b = param<PARAM>(p.beta, c);
+            }
             float f[8], o[8];
             unpack8<X_FP16>(v[u], f);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float t = __builtin_fmaf((f[j] - mean) * rstd, g, b);
+                const float t = __builtin_fmaf(f[j] - mean, a, b);
                 o[j] = t * __builtin_amdgcn_rcpf(1.0f + __expf(-t));
             }
             store16<true>(yq + (int64_t)i * kVec, pack8<X_FP16>(o));
@@ -210,19 +238,33 @@ __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
     const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
     const int nv = chunk_vectors<VPT>(p, k);
+    const float* part = p.partial + 2 * q * p.chunks;
+    const float last_n = (float)(p.group_size - (int64_t)(p.chunks - 1) * kChunk);
+    // This thread's first partial is read before the chunk, so that the
+    // combine (two workgroup reductions) runs while the chunk is in flight.
+    const int i0 = threadIdx.x;
+    const bool has0 = i0 < p.chunks;
+    f32x2 first = {0.0f, 0.0f};
+    if (has0)
+        first = *reinterpret_cast<const f32x2*>(part + 2 * i0);
     u32x4 v[VPT];
     load_chunk<true>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
 
-    const float* part = p.partial + 2 * q * p.chunks;
-    const float last_n = (float)(p.group_size - (int64_t)(p.chunks - 1) * kChunk);
-    float s = 0.0f;
-    for (int i = threadIdx.x; i < p.chunks; i += kBlock) {
+    // Same order in every workgroup of the group: thread sums over
+    // i = tid, tid + 256, ..., then the fixed-order workgroup reduction.
+    const float n0 = i0 == p.chunks - 1 ? last_n : (float)kChunk;
+    float s = has0 ? n0 * first[0] : 0.0f;
+    for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
         const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
         s = __builtin_fmaf(n_i, part[2 * i], s);
     }
     const float mean = block_sum<kWaves>(s, red[0]) / (float)p.group_size;
     float m2 = 0.0f;
-    for (int i = threadIdx.x; i < p.chunks; i += kBlock) {
+    if (has0) {
+        const float d = first[0] - mean;
+        m2 = __builtin_fmaf(n0 * d, d, first[1]);
+    }
+    for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
         const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
         const float d = part[2 * i] - mean;
         m2 += __builtin_fmaf(n_i * d, d, part[2 * i + 1]);
