@@ -218,6 +218,21 @@ def test_flux_workload_separate_q_k(x_dtype):
     print("flux", x_dtype, "max_abs", mq, mk)
 
 
+@pytest.mark.parametrize("key", ["shard_tokens", "shard_heads"])
+def test_headline_shards(key):
+    """One GPU's share of the headline over 8 GPUs, in full against the oracle:
+    the last token shard (tokens 28665..32759 with their own positions) and a
+    5-head shard of all 32760 tokens; V untouched."""
+    w = wl.WORKLOADS[key]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, "interleaved")
+    out = run_fused(qkv, qg, kg, cos, sin, "interleaved")
+    m = compare_fused(out, qkv, "bf16", H, D, qg, kg, cos, sin, "interleaved", what=key)
+    print(key, "max_abs", m)
+
+
 def _sample_windows(T, rng, n=12, width=48):
     starts = sorted(set(rng.integers(0, T - width, n).tolist()))
     wins = [(0, width)] + [(s, s + width) for s in starts] + [(T - width - 3, T)]

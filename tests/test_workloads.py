@@ -15,6 +15,10 @@ def test_algorithmic_bytes_of_each_workload():
     assert b(32760, 40, 128) == 1_375_395_840
     assert b(75600, 40, 128) == 3_173_990_400
     assert b(75600, 40, 128, cos_layout="per_head") == 6_193_152_000
+    # the headline's shards over 8 GPUs: by tokens, and by heads (the shared
+    # row then serves 10 Q+K heads instead of 80)
+    assert b(4095, 40, 128) == 1_375_395_840 // 8
+    assert b(32760, 5, 128) == 32760 * 10 * 128 * 4 + 32760 * 128 * 8
 
 
 @pytest.mark.parametrize("key", sorted(wl.WORKLOADS))
@@ -23,6 +27,12 @@ def test_positions_cover_the_grid(key):
     pos = wl.positions(w)
     assert pos.shape == (w.tokens, len(w.grid))
     assert 2 * sum(w.split) == w.head_dim
+    if w.token_begin:
+        # a token shard: its slice of the whole grid's sequence
+        full = wl.grid_positions(w.grid, w.text_tokens)
+        assert np.array_equal(pos, full[w.token_begin:w.token_begin + w.tokens])
+        assert w.token_begin + w.tokens <= full.shape[0]
+        return
     assert np.all(pos[: w.text_tokens] == 0)
     img = pos[w.text_tokens:]
     for a, n in enumerate(w.grid):

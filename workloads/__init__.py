@@ -56,6 +56,7 @@ class Workload:
     grid: tuple              # position grid (row-major), one entry per axis
     split: tuple             # frequency pairs per axis; sums to head_dim / 2
     text_tokens: int = 0     # leading tokens all at position 0 on every axis
+    token_begin: int = 0     # first token of the grid's sequence this workload holds (a shard)
     note: str = field(default="", compare=False)
 
 
@@ -77,6 +78,16 @@ WORKLOADS = {
         "large", 1005, "fused", 75600, 40, 128, ("bf16",),
         ("interleaved", "rotate_half"), ("shared", "per_head"), (21, 45, 80), (22, 21, 21),
         note="21x45x80 latent grid"),
+    # What one GPU of eight runs when the headline is sharded (the pass needs
+    # no exchange): the last token shard, or one head shard of every token.
+    "shard_tokens": Workload(
+        "shard_tokens", 1006, "fused", 4095, 40, 128, ("bf16",), ("interleaved",),
+        ("shared",), (21, 30, 52), (22, 21, 21), token_begin=7 * 4095,
+        note="tokens 28665..32759 of the Wan 21x30x52 grid: the last of 8 token shards"),
+    "shard_heads": Workload(
+        "shard_heads", 1007, "fused", 32760, 5, 128, ("bf16",), ("interleaved",),
+        ("shared",), (21, 30, 52), (22, 21, 21),
+        note="Wan 21x30x52 grid, 5 of the 40 heads of Q, K and V: one of 8 head shards"),
 }
 
 
@@ -95,8 +106,9 @@ def grid_positions(grid: tuple, text_tokens: int = 0) -> np.ndarray:
 
 
 def positions(w: Workload) -> np.ndarray:
-    """Integer positions [tokens, n_axes], row-major over ``w.grid``."""
-    pos = grid_positions(w.grid, w.text_tokens)
+    """Integer positions [tokens, n_axes], row-major over ``w.grid``, from
+    token ``w.token_begin`` of that sequence on."""
+    pos = grid_positions(w.grid, w.text_tokens)[w.token_begin:w.token_begin + w.tokens]
     assert pos.shape[0] == w.tokens, (pos.shape, w.tokens)
     return pos
 
