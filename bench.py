@@ -518,7 +518,7 @@ def main():
     info = qkr.kernel_info(D, args.layout,
                            qkr.binding.QKR_BF16 if cos_bytes == 2 else qkr.binding.QKR_FP32, style,
                            qkr.binding.QKR_FP16 if dtype == "fp16" else qkr.binding.QKR_BF16,
-                           heads=H, tokens=T)
+                           heads=H, tokens=T, tensors="fused" if w.layout == "fused" else "pair")
 
     traffic = measured_traffic(args.workload, args.layout, style)
     result = {

@@ -24,9 +24,11 @@ QKR_ERR_WORKSPACE = -8
 QKR_BF16, QKR_FP16, QKR_FP32 = 0, 1, 2
 QKR_COS_SHARED, QKR_COS_PER_HEAD = 0, 1
 QKR_ROPE_INTERLEAVED, QKR_ROPE_ROTATE_HALF = 0, 1
+QKR_TENSORS_FUSED, QKR_TENSORS_PAIR, QKR_TENSORS_ONE = 0, 1, 2
 
 LAYOUTS = {"shared": QKR_COS_SHARED, "per_head": QKR_COS_PER_HEAD}
 STYLES = {"interleaved": QKR_ROPE_INTERLEAVED, "rotate_half": QKR_ROPE_ROTATE_HALF}
+TENSORS = {"fused": QKR_TENSORS_FUSED, "pair": QKR_TENSORS_PAIR, "one": QKR_TENSORS_ONE}
 EXPORTS = ("qknorm_rope_fused", "qknorm_rope_strerror", "qknorm_rope_version",
            "qknorm_rope_kernel_info", "dit_fuse_scale_shift",
            "dit_group_norm_silu_workspace_size", "dit_group_norm_silu")
@@ -69,7 +71,7 @@ def load_library(path: str = LIB_PATH):
     lib.qknorm_rope_strerror.restype = ctypes.c_char_p
     lib.qknorm_rope_version.argtypes = []
     lib.qknorm_rope_version.restype = ctypes.c_int
-    lib.qknorm_rope_kernel_info.argtypes = [i32, i32, i64, i32, i32, i32, i32,
+    lib.qknorm_rope_kernel_info.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32,
                                             ctypes.POINTER(KernelInfo)]
     lib.qknorm_rope_kernel_info.restype = ctypes.c_int
     lib.dit_fuse_scale_shift.argtypes = [vp, vp, i64, i32, i64, vp, vp, i32, f32, i32, vp]
@@ -224,12 +226,16 @@ def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
 
 def kernel_info(head_dim: int = 128, cos_layout: str = "shared", cos_dtype: int = QKR_FP32,
                 style: str = "interleaved", dtype: int = QKR_BF16, heads: int = 40,
-                tokens: int = 32760) -> dict:
-    """Registers, LDS, scratch and schedule of the kernel a fused-QKV call launches."""
+                tokens: int = 32760, tensors: str = "fused") -> dict:
+    """Registers, LDS, scratch and schedule of the kernel a call launches.
+
+    ``tensors``: "fused" (one QKV buffer), "pair" (separate q and k) or "one"
+    (q or k alone).
+    """
     info = KernelInfo()
-    _check(load_library().qknorm_rope_kernel_info(head_dim, heads, tokens, LAYOUTS[cos_layout],
-                                                  cos_dtype, STYLES[style], dtype,
-                                                  ctypes.byref(info)))
+    _check(load_library().qknorm_rope_kernel_info(head_dim, heads, tokens, TENSORS[tensors],
+                                                  LAYOUTS[cos_layout], cos_dtype, STYLES[style],
+                                                  dtype, ctypes.byref(info)))
     return {name: getattr(info, name) for name, _ in KernelInfo._fields_}
 
 

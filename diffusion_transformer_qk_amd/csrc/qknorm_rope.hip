@@ -546,17 +546,20 @@ extern "C" const char* qknorm_rope_strerror(int status)
 extern "C" int qknorm_rope_version(void) { return QKNORM_ROPE_VERSION; }
 
 extern "C" int qknorm_rope_kernel_info(int32_t head_dim, int32_t heads, int64_t tokens,
-                                       int32_t cos_layout, int32_t cos_dtype, int32_t style,
-                                       int32_t dtype, qkr_kernel_info* out)
+                                       int32_t tensors, int32_t cos_layout, int32_t cos_dtype,
+                                       int32_t style, int32_t dtype, qkr_kernel_info* out)
 {
     if (!out)
         return QKR_ERR_NULL;
+    if (tensors != QKR_TENSORS_FUSED && tensors != QKR_TENSORS_PAIR && tensors != QKR_TENSORS_ONE)
+        return QKR_ERR_ARG;
     const int cfg = check_config(head_dim, cos_layout, cos_dtype, style, dtype);
     if (cfg != QKR_OK)
         return cfg;
     if (tokens < 0 || tokens >= QKR_MAX_TOKENS || heads < 1 || heads > QKR_MAX_HEADS)
         return QKR_ERR_SHAPE;
-    const Launch l = plan_launch(head_dim, heads, tokens, 2, false, cos_layout == QKR_COS_PER_HEAD);
+    const Launch l = plan_launch(head_dim, heads, tokens, tensors == QKR_TENSORS_ONE ? 1 : 2,
+                                 tensors == QKR_TENSORS_PAIR, cos_layout == QKR_COS_PER_HEAD);
     hipFuncAttributes attr;
     KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype, l);
     if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn)) != hipSuccess)

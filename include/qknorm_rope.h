@@ -115,16 +115,24 @@ typedef struct {
     int32_t die_runs;         /* 1: each die processes one contiguous token run   */
 } qkr_kernel_info;
 
+/* Which tensors a call passes, for qknorm_rope_kernel_info. */
+enum {
+    QKR_TENSORS_FUSED = 0,    /* qkv: one fused [tokens, 3*heads*head_dim] buffer */
+    QKR_TENSORS_PAIR = 1,     /* q and k, two separate buffers                     */
+    QKR_TENSORS_ONE = 2       /* q or k alone                                      */
+};
+
 /*
  * qknorm_rope_kernel_info -- fill *out for the kernel that qknorm_rope_fused
- * launches on a fused QKV buffer of `tokens` x 3*`heads`*`head_dim` with the
- * given layout and dtypes (the unroll depth and block order depend on heads
- * and tokens).  Needs a HIP device (queries the loaded code object).
- * Returns QKR_OK, QKR_ERR_NULL, QKR_ERR_ARG / QKR_ERR_UNSUPPORTED /
- * QKR_ERR_SHAPE for a bad configuration, or QKR_ERR_HIP.
+ * launches for `tokens` tokens of `heads` heads of `head_dim`, with the
+ * tensors given as `tensors` (QKR_TENSORS_*) and the given layout and dtypes
+ * (the unroll depth and block order depend on heads, tokens and tensors).
+ * Needs a HIP device (queries the loaded code object).  Returns QKR_OK,
+ * QKR_ERR_NULL, QKR_ERR_ARG / QKR_ERR_UNSUPPORTED / QKR_ERR_SHAPE for a bad
+ * configuration (checked before any HIP call), or QKR_ERR_HIP.
  */
-int qknorm_rope_kernel_info(int32_t head_dim, int32_t heads, int64_t tokens, int32_t cos_layout,
-                            int32_t cos_dtype, int32_t style, int32_t dtype,
+int qknorm_rope_kernel_info(int32_t head_dim, int32_t heads, int64_t tokens, int32_t tensors,
+                            int32_t cos_layout, int32_t cos_dtype, int32_t style, int32_t dtype,
                             qkr_kernel_info* out);
 
 #ifdef __cplusplus

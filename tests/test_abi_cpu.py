@@ -125,6 +125,22 @@ def test_zero_tokens_is_a_no_op():
     assert call(tokens=0, head_dim=32) == b.QKR_ERR_UNSUPPORTED
 
 
+def test_kernel_info_rejects_bad_arguments_before_any_hip_call():
+    lib = b.load_library()
+    info = b.KernelInfo()
+    ref = ctypes.byref(info)
+    assert lib.qknorm_rope_kernel_info(128, 40, 100, 3, 0, b.QKR_FP32, 0, b.QKR_BF16, ref) \
+        == b.QKR_ERR_ARG                                          # tensors out of range
+    assert lib.qknorm_rope_kernel_info(128, 40, 100, -1, 0, b.QKR_FP32, 0, b.QKR_BF16, ref) \
+        == b.QKR_ERR_ARG
+    assert lib.qknorm_rope_kernel_info(128, 40, 100, 0, 0, b.QKR_FP32, 0, b.QKR_BF16, None) \
+        == b.QKR_ERR_NULL
+    assert lib.qknorm_rope_kernel_info(96, 40, 100, 1, 0, b.QKR_FP32, 0, b.QKR_BF16, ref) \
+        == b.QKR_ERR_UNSUPPORTED
+    assert lib.qknorm_rope_kernel_info(128, 40, 1 << 24, 2, 0, b.QKR_FP32, 0, b.QKR_BF16, ref) \
+        == b.QKR_ERR_SHAPE
+
+
 def test_separate_mode_skips_missing_tensor_gamma():
     # k absent: its gamma may be NULL; the call is then only rejected for the table
     assert call(qkv=0, q=A, k=0, k_gamma=0, cos=0) == b.QKR_ERR_NULL

@@ -167,6 +167,22 @@ def test_kernels_do_not_spill(head_dim, layout):
     assert {(u, o) for u in depths for o in (0, 1)} <= seen, seen
 
 
+def test_kernel_info_follows_the_tensors_passed():
+    """The schedule kernel_info reports for each way of passing the tensors:
+    two tokens per workgroup for fused QKV or a q, k pair, four for a single
+    tensor; per-die token runs for one streamed buffer only."""
+    args = (128, "shared", qkr.binding.QKR_FP32, "interleaved", qkr.binding.QKR_BF16)
+    fused = qkr.kernel_info(*args, heads=40, tokens=100000, tensors="fused")
+    pair = qkr.kernel_info(*args, heads=40, tokens=100000, tensors="pair")
+    one = qkr.kernel_info(*args, heads=40, tokens=100000, tensors="one")
+    assert (fused["tokens_per_block"], fused["die_runs"]) == (2, 1)
+    assert (pair["tokens_per_block"], pair["die_runs"]) == (2, 0)
+    assert (one["tokens_per_block"], one["die_runs"]) == (4, 1)
+    assert fused["heads_in_flight"] == pair["heads_in_flight"] == one["heads_in_flight"] == 10
+    small = qkr.kernel_info(*args, heads=40, tokens=1000, tensors="one")
+    assert small["die_runs"] == 0
+
+
 # ----------------------------------------------------------------------------- the five workloads
 
 
