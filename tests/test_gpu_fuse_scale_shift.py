@@ -213,6 +213,7 @@ def test_byte_offsets_beyond_4gib_in_place():
     qkr.fuse_scale_shift(x, sc.to(DEV), sh.to(DEV), out=x, rows_per_batch=rows)
     torch.cuda.synchronize()
     samples = [0, 1, 1023, 1024, 209715, 419429, 419430, 419431, rows - 1]
+    assert max(samples) < rows
     idx = torch.tensor(samples)
     xs = block[idx % B]
     y, n = oracle_rows(xs, "bf16", sc, sh, len(samples), wl.EPS)
@@ -310,6 +311,7 @@ def test_maximum_rows():
     rng = np.random.default_rng(4748)
     samples = sorted({0, 1, B, rpb - 1, rpb, 2 * rpb - 1, 2 * rpb, rows // 2, rows - 2,
                       rows - 1, *rng.integers(0, rows, 20).tolist()})
+    assert max(samples) < rows
     got_all = _decode(y[torch.tensor(samples, device=DEV)], "bf16")
     m = 0.0
     for i, r in enumerate(samples):

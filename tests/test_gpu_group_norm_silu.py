@@ -320,6 +320,7 @@ def test_maximum_workgroups():
     torch.cuda.synchronize()
     rng = np.random.default_rng(4950)
     samples = sorted({0, 1, B - 1, B, n // 2, n - 2, n - 1, *rng.integers(0, n, 20).tolist()})
+    assert max(samples) < n
     got_all = _decode(y.view(n, -1)[torch.tensor(samples, device=DEV)], "bf16")
     m = 0.0
     for i, q in enumerate(samples):

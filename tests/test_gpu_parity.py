@@ -350,6 +350,7 @@ def test_byte_offsets_beyond_4gib():
         n = min(B, T - i)
         assert torch.equal(x[i:i + n, 2 * H * D:], blk[:n, 2 * H * D:]), "V changed"
     samples = [0, 1, B - 1, B, 69905, 139809, 139810, 139811, T - 2, T - 1]
+    assert max(samples) < T
     idx = torch.tensor(samples)
     rows = block[idx % B]
     q_ref, k_ref = oracle_fused(rows, "bf16", H, D, qg, kg, cos[idx], sin[idx], "interleaved")
@@ -607,7 +608,8 @@ def _repeat_rows(block_dev: torch.Tensor, total: int) -> torch.Tensor:
     b = block_dev.shape[0]
     out = torch.empty((total, block_dev.shape[1]), dtype=block_dev.dtype, device=DEV)
     n = total // b
-    out[:n * b].view(n, b, -1).copy_(block_dev.unsqueeze(0).expand(n, -1, -1))
+    if n:
+        out[:n * b].view(n, b, -1).copy_(block_dev.unsqueeze(0).expand(n, -1, -1))
     out[n * b:].copy_(block_dev[:total - n * b])
     return out
 
@@ -639,6 +641,7 @@ def test_maximum_tokens():
     rng = np.random.default_rng(4546)
     samples = sorted({0, 1, B - 1, B, T // 2, T - B, T - 2, T - 1,
                       *rng.integers(0, T, 24).tolist()})
+    assert max(samples) < T
     idx = torch.tensor(samples)
     rows = block[idx % B]
     q_ref, k_ref = oracle_fused(rows, "bf16", H, D, qg, kg, cos[idx % B], sin[idx % B],
@@ -647,3 +650,61 @@ def test_maximum_tokens():
     m = max(check_close(got[:, 0], q_ref, "bf16", "max tokens Q"),
             check_close(got[:, 1], k_ref, "bf16", "max tokens K"))
     print("maximum tokens max_abs", m)
+
+
+# heads giving each unroll depth (head iterations in flight), per head_dim
+SWEEP_HEADS = {128: {3: 5, 6: 20, 10: 40, 12: 48}, 64: {3: 9, 6: 44, 10: 72, 12: 100}}
+CODES = {"bf16": qkr.binding.QKR_BF16, "fp16": qkr.binding.QKR_FP16, "fp32": qkr.binding.QKR_FP32}
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("layout", ["shared", "per_head"])
+@pytest.mark.parametrize("table", ["fp32", "bf16"])
+@pytest.mark.parametrize("x_dtype", ["bf16", "fp16"])
+def test_every_kernel_instantiation(head_dim, layout, table, x_dtype):
+    """Every compiled kernel of one (head_dim, layout, table dtype, data dtype):
+    both styles, each unroll depth and both block orders (203 tokens: hardware
+    order; 8200 tokens = 4100 workgroups: per-die runs with a ragged
+    remainder), against the oracle on sampled tokens, V checked on them too.
+    Per-head tables hold a distinct row per (token, head).  Activations and
+    tables repeat a 256-token block (the pass is per token)."""
+    D, B = head_dim, 256
+    depths = (3, 6, 10) if layout == "per_head" else (3, 6, 10, 12)
+    hit = set()
+    rng = np.random.default_rng(5000 + D)
+    for style in ("interleaved", "rotate_half"):
+        for depth in depths:
+            H = SWEEP_HEADS[D][depth]
+            block = wl.fused_qkv(5000 + H, B, H, D, x_dtype)
+            qg, kg = wl.norm_weights(5000 + H, D)
+            if layout == "shared":
+                cos, sin = tables(np.arange(B) * 3 + 1, (D // 2,), D, style, dtype=table)
+            else:
+                c, s = tables(np.arange(B * H) + 1, (D // 2,), D, style, dtype=table)
+                cos, sin = c.view(B, H, D), s.view(B, H, D)
+            blk = block.to(DEV)
+            for T in (203, 8200):
+                info = qkr.kernel_info(D, layout, CODES[table], style, CODES[x_dtype], heads=H,
+                                       tokens=T)
+                hit.add((style, info["heads_in_flight"], info["die_runs"]))
+                x = _repeat_rows(blk, T)
+                cd = _repeat_rows(dev(cos).reshape(B, -1), T).view(T, *cos.shape[1:])
+                sd = _repeat_rows(dev(sin).reshape(B, -1), T).view(T, *sin.shape[1:])
+                qkr.qknorm_rope_fused(x, q_gamma=dev(qg), k_gamma=dev(kg), cos=cd, sin=sd,
+                                      style=style, cos_layout=layout)
+                torch.cuda.synchronize()
+                idx = sorted(i for i in {0, 1, B - 1, B, T // 2, T - 2, T - 1,
+                                         *rng.integers(0, T, 8).tolist()} if i < T)
+                assert 0 <= idx[0] and idx[-1] < T     # checked here, before indexing on the GPU
+                it = torch.tensor(idx)
+                rows = block[it % B]
+                q_ref, k_ref = oracle_fused(rows, x_dtype, H, D, qg, kg, cos[it % B],
+                                            sin[it % B], style, layout)
+                out = x[it.to(DEV)].cpu()
+                got = _decode(out, x_dtype).reshape(len(idx), 3, H, D)
+                what = "%s U%d order%d T%d" % (style, info["heads_in_flight"], info["die_runs"], T)
+                check_close(got[:, 0], q_ref, x_dtype, what + " Q")
+                check_close(got[:, 1], k_ref, x_dtype, what + " K")
+                assert_v_untouched(out, rows, H, D)
+    assert hit == {(st, u, o) for st in ("interleaved", "rotate_half") for u in depths
+                   for o in (0, 1)}, hit
