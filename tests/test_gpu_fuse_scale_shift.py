@@ -320,3 +320,48 @@ def test_maximum_rows():
         m = max(m, check_rows(got_all[i:i + 1], yr, nr, sc[b:b + 1], sh[b:b + 1], 1, 0, "bf16",
                               "row %d" % r))
     print("maximum rows max_abs", m)
+
+
+@pytest.mark.parametrize("dtype,mod", [("bf16", "fp32"), ("bf16", "bf16"), ("bf16", "fp16"),
+                                       ("fp16", "fp32"), ("fp16", "bf16"), ("fp16", "fp16")])
+def test_every_kernel_instantiation(dtype, mod):
+    """Every compiled kernel of one (data, modulation) dtype pair: 2..16 row
+    vectors per lane, rows of exactly that many vectors and rows 8 elements
+    short (tail masks), one-row workgroups (203 rows) and workgroups of 4
+    staging the modulation (8200 rows), each over batches that split inside a
+    workgroup.  Sampled rows against the oracle.  Rows repeat a 256-row block
+    (the step is per row)."""
+    B = 256
+    rng = np.random.default_rng(6000)
+    hit = set()
+    for vpl in range(2, 17, 2):
+        for hidden in (vpl * 512, vpl * 512 - 8):
+            block, sc3, sh3 = wl.adaln_inputs(6000 + hidden, B, hidden, 3, dtype, mod)
+            blk = block.to(DEV)
+            for rows, rpb in ((203, 101), (8200, 4099)):
+                batches = -(-rows // rpb)
+                sc, sh = sc3[:batches], sh3[:batches]
+                n = rows // B
+                x = torch.empty((rows, hidden), dtype=blk.dtype, device=DEV)
+                if n:
+                    x[:n * B].view(n, B, hidden).copy_(blk.unsqueeze(0).expand(n, -1, -1))
+                x[n * B:].copy_(blk[:rows - n * B])
+                y = qkr.fuse_scale_shift(x, sc.to(DEV), sh.to(DEV), rows_per_batch=rpb)
+                torch.cuda.synchronize()
+                # the dispatch rule: vectors per lane, whole rows of them, staged schedule
+                hit.add((vpl, hidden == vpl * 512, rows >= 8192))
+                samples = sorted(r for r in {0, 1, 2, 3, rpb - 1, rpb, rows // 2, rows - 2,
+                                             rows - 1, *rng.integers(0, rows, 6).tolist()}
+                                 if r < rows)
+                assert samples[-1] < rows          # checked before indexing on the GPU
+                got_all = _decode(y[torch.tensor(samples, device=DEV)], dtype)
+                refs = [oracle_rows(block[r % B:r % B + 1], dtype, sc[r // rpb:r // rpb + 1],
+                                    sh[r // rpb:r // rpb + 1], 1, wl.EPS) for r in samples]
+                bsel = torch.tensor([r // rpb for r in samples])
+                # one row of modulation per sampled row; the RNE-agreement
+                # fraction is taken over all of the case's sampled rows
+                check_rows(got_all, np.concatenate([a for a, _ in refs]),
+                           np.concatenate([b for _, b in refs]), sc[bsel], sh[bsel], 1, 0, dtype,
+                           "hidden %d rows %d" % (hidden, rows))
+    assert hit == {(v, f, s) for v in range(2, 17, 2) for f in (True, False)
+                   for s in (True, False)}

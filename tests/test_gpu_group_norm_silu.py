@@ -328,3 +328,45 @@ def test_maximum_workgroups():
                             q % B, q % B + 1)
         m = max(m, check_groups(got_all[i], ref, spatial, "bf16", "group %d" % q))
     print("maximum workgroups max_abs", m)
+
+
+# (n, channels, spatial, groups, vectors per thread or 0 for one chunk per group)
+GN_SWEEP = [
+    (2, 64, 512, 32, 0),            # 1,024-element groups: the single-read kernel
+    (4, 512, 16384, 32, 8),         # channels of exactly one 16,384-element chunk
+    (4, 512, 16392, 32, 8),         # channel boundaries inside chunks (two-channel select)
+    (64, 512, 1000, 8, 8),          # channels shorter than a chunk (per-vector division)
+    (2, 512, 16384, 32, 4),         # 2,048 workgroups only with 8,192-element chunks
+    (1, 512, 16384, 32, 2),         # ... only with 4,096-element chunks
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("param", ["fp32", "bf16", "fp16"])
+def test_every_kernel_instantiation(dtype, param):
+    """Every compiled kernel of one (data, affine) dtype pair: the single-read
+    kernel, and the stats + apply pair at each chunk size, with channels
+    longer and shorter than a chunk.  The chunk size is confirmed through the
+    workspace size it implies; sampled groups against the oracle.  Samples
+    repeat a block of at most 2 (the step is per group)."""
+    for n, channels, spatial, groups, vpt in GN_SWEEP:
+        gsize = channels // groups * spatial
+        chunk = 2048 * vpt
+        want_ws = 0 if vpt == 0 else n * groups * -(-gsize // chunk) * 8
+        assert qkr.group_norm_silu_workspace_size(n, channels, spatial, groups) == want_ws
+        nb = min(n, 2)
+        block, g, b = wl.gn_inputs(7000 + spatial + n, nb, channels, spatial, dtype, param)
+        blk = block.to(DEV)
+        x = blk.repeat(n // nb, 1, 1)
+        y = qkr.group_norm_silu(x, g.to(DEV), b.to(DEV), groups)
+        torch.cuda.synchronize()
+        flat = y.reshape(-1)
+        got, ref = [], []
+        for q in sorted({0, 1, n * groups // 2 + 1, n * groups - 1}):
+            qb = q % (nb * groups)
+            ref.append(oracle_groups(block, dtype, channels, spatial, groups, g, b, wl.EPS, qb,
+                                     qb + 1))
+            got.append(_decode(flat[q * gsize:(q + 1) * gsize], dtype))
+        # per-group bounds; the RNE-agreement fraction over all sampled groups
+        check_groups(np.concatenate(got), np.concatenate(ref), gsize, dtype,
+                     "%s vpt %d" % ((n, channels, spatial, groups), vpt))
