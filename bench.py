@@ -19,7 +19,7 @@ oracle on a bounded sample of the same workload.
                   [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                   [--layout shared|per_head] [--style interleaved|rotate_half]
-                  [--dtype bf16|fp16] [--flush] [--no-cpu-baseline] [--calib-copy]
+                  [--dtype bf16|fp16] [--flush] [--graph] [--no-cpu-baseline] [--calib-copy]
 
 Other workloads (tiny, mid, flux, large) are reported the same way; with
 --flush a 1 GiB buffer is rewritten before every timed call (outside that
@@ -108,6 +108,9 @@ def parse():
                     help="budget for the CPU-oracle sample")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="QK pass: also time calls replayed from a HIP graph of 20 "
+                         "back-to-back launches (no per-launch host cost)")
     return ap.parse_args()
 
 
@@ -124,6 +127,31 @@ def calib_copy(steps: int):
     dt = (time.perf_counter() - t0) / steps
     print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
                       "copy_GBps": round(2 * n / dt / 1e9, 1), "steps": steps}))
+
+
+def graph_call_us(launch, stream, steps: int, per_graph: int = 20) -> float:
+    """Mean µs per call when `per_graph` back-to-back calls are replayed from
+    one captured HIP graph (at least `steps` calls in all)."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(per_graph):
+            launch()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()                      # warm
+    reps = max(1, -(-steps // per_graph))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e3 / (reps * per_graph)
 
 
 def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
@@ -511,6 +539,7 @@ def main():
 
     region_ms = region0.elapsed_time(region1)
     per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3   # µs
+    graph_us = graph_call_us(launch, stream, K) if args.graph and not args.flush else None
     mean_us = float(per.mean())
     achieved = nbytes / (mean_us * 1e-6) / 1e9
     # with flushing, the region also holds the flush writes: use the call times
@@ -552,6 +581,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic},
     }
+    if graph_us is not None:
+        result["graph_us_per_call"] = round(graph_us, 2)
     if (not args.no_cpu_baseline and qkv_cpu is not None and args.layout == "shared"
             and args.cos_dtype == "fp32"):
         result["cpu_baseline"] = cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style,
