@@ -4,6 +4,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -29,9 +31,6 @@ def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch)
     with open(path, "w") as f:
         json.dump(rec, f)
     assert bench.measured_traffic("headline", "shared", "interleaved") is None
-
-
-import pytest  # noqa: E402
 
 
 @pytest.mark.parametrize("op,key", [("fuse_scale_shift", "adaln_wan/bf16/fp32/out"),
