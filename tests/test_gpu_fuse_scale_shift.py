@@ -20,6 +20,7 @@ import torch
 import diffusion_transformer_qk_amd as qkr
 import oracle
 import workloads as wl
+from tests.gpu_common import decode as _decode, same_bits, ulp as _ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -27,19 +28,6 @@ DEV = torch.device("cuda:0")
 PAD = 4096
 CANARY = 0x6A1B
 FP32_NOISE = 8e-6
-
-
-def _decode(t, dtype):
-    bits = wl.u16(t.cpu())
-    if dtype == "fp16":
-        return bits.view(np.float16).astype(np.float64)
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def _ulp(v, dtype):
-    p, emin = (11, -14) if dtype == "fp16" else (8, -126)
-    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
-    return 2.0 ** (e - p + 1)
 
 
 def _mod_np(t):
@@ -89,11 +77,6 @@ def guarded_empty(shape, dtype):
 
 def canaries_intact(buf):
     return bool((buf[:PAD] == CANARY).all()) and bool((buf[-PAD:] == CANARY).all())
-
-
-def same_bits(a, b):
-    view = torch.int32 if a.dtype == torch.float32 else torch.int16
-    return a.dtype == b.dtype and torch.equal(a.view(view), b.view(view))
 
 
 def run(x, sc, sh, rows_per_batch=None, eps=wl.EPS, inplace=False):

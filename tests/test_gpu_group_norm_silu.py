@@ -16,6 +16,7 @@ import torch
 import diffusion_transformer_qk_amd as qkr
 import oracle
 import workloads as wl
+from tests.gpu_common import decode as _decode, same_bits, ulp as _ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -25,30 +26,12 @@ CANARY = 0x5C3D
 FP32_NOISE = 8e-6
 
 
-def _decode(t, dtype):
-    bits = wl.u16(t.cpu())
-    if dtype == "fp16":
-        return bits.view(np.float16).astype(np.float64)
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def _ulp(v, dtype):
-    p, emin = (11, -14) if dtype == "fp16" else (8, -126)
-    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
-    return 2.0 ** (e - p + 1)
-
-
 def _pnp(t):
     return t.numpy() if t.dtype == torch.float32 else wl.u16(t)
 
 
 def _pname(t):
     return {torch.float32: "fp32", torch.bfloat16: "bf16", torch.float16: "fp16"}[t.dtype]
-
-
-def same_bits(a, b):
-    view = torch.int32 if a.dtype == torch.float32 else torch.int16
-    return a.dtype == b.dtype and torch.equal(a.view(view), b.view(view))
 
 
 def check_groups(got, ref, gsize, dtype, what, rne_check=True):

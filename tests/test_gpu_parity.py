@@ -15,6 +15,7 @@ import torch
 import diffusion_transformer_qk_amd as qkr
 import oracle
 import workloads as wl
+from tests.gpu_common import decode as _decode, ulp as _ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -23,21 +24,6 @@ MISMATCH_FRAC = {"bf16": 1e-3, "fp16": 2e-3}
 DEV = torch.device("cuda:0")
 PAD = 4096          # canary elements on each side of a tensor
 CANARY = 0x7E5A
-
-
-def _decode(t: torch.Tensor, dtype: str) -> np.ndarray:
-    bits = wl.u16(t.cpu())
-    if dtype == "fp16":
-        return bits.view(np.float16).astype(np.float64)
-    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-def _ulp(v: np.ndarray, dtype: str) -> np.ndarray:
-    p, emin = (11, -14) if dtype == "fp16" else (8, -126)
-    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** emin)))
-    return 2.0 ** (e - p + 1)
-
-
 FP32_NOISE = 8e-6   # fp32 math error, relative to the largest |o| of the head
 
 
