@@ -37,16 +37,36 @@ def hipcc() -> str:
     return path
 
 
+OBJ_DIR = os.path.join(PKG, "_build")
+
+
 def build(save_temps: str | None = None) -> str:
-    """Build the library in-tree and return its path."""
+    """Build the library in-tree and return its path.
+
+    Each source compiles to its own object in parallel (they share no device
+    code), then one link makes the shared library.  With ``save_temps`` the
+    whole build runs as one hipcc call that keeps its ISA/IR there.
+    """
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
-    cwd = None
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
-        cmd.insert(1, "--save-temps")
-        cwd = save_temps
-    subprocess.run(cmd, check=True, cwd=cwd)
+        cmd = [hipcc(), "--save-temps", *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
+        subprocess.run(cmd, check=True, cwd=save_temps)
+        os.replace(tmp, LIB)
+        return LIB
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src in SRCS:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        objs.append(obj)
+        procs.append((src, subprocess.Popen([hipcc(), *compile_flags, "-I", INCLUDE, "-c", src,
+                                             "-o", obj])))
+    failed = [src for src, proc in procs if proc.wait() != 0]
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(failed))
+    subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp],
+                   check=True)
     os.replace(tmp, LIB)
     return LIB
 
