@@ -20,10 +20,12 @@
 //     are formed once per token (shared) or per head (per-head layout) with
 //     the same instructions, so both layouts give bit-identical output;
 //   * sum of squares: in-lane fma chain, then a DPP butterfly across the
-//     head's lanes (quad_perm xor1 / xor2, row_half_mirror, row_mirror) that
+//     head's lanes (quad_perm xor1 / xor2, row_half_mirror, row_mirror, and
+//     for D = 256 a ds_swizzle xor 16 across the two 16-lane rows) that
 //     leaves the identical sum in every lane of the head;
 //   * rotate-half partners sit D/2 elements away = half the head's lanes:
-//     exchanged with DPP row_ror:8 (D = 128) or ds_swizzle xor 4 (D = 64);
+//     exchanged with DPP row_ror:8 (D = 128) or ds_swizzle xor 4 / xor 16
+//     (D = 64 / 256);
 //   * fp32 -> bf16/fp16 with the packed round-to-nearest-even converts.
 #include <hip/hip_runtime.h>
 
@@ -57,16 +59,27 @@ struct Params {
 
 // ---------------------------------------------------------------- lane helpers
 
-// Sum over the L lanes of one head (L = 8 or 16, aligned groups).  Each step
-// adds the same two partial sums in every lane, so all lanes end bit-equal.
+// Value of lane ^ 16 (within each 32-lane half of the wave): ds_swizzle in
+// bit mode with and-mask 0x1F and xor-mask 0x10.
+__device__ __forceinline__ float lane_xor16(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                 0x401F));
+}
+
+// Sum over the L lanes of one head (L = 8, 16 or 32, aligned groups).  Each
+// step adds the same two partial sums in every lane, so all lanes end
+// bit-equal.
 template <int L>
 __device__ __forceinline__ float head_sum(float v)
 {
     v += dpp<0xB1>(v);       // quad_perm [1,0,3,2]
     v += dpp<0x4E>(v);       // quad_perm [2,3,0,1]
     v += dpp<0x141>(v);      // row_half_mirror: the other quad of the 8-lane half
-    if constexpr (L == 16)
+    if constexpr (L >= 16)
         v += dpp<0x140>(v);  // row_mirror: the other half of the 16-lane row
+    if constexpr (L == 32)
+        v += lane_xor16(v);  // the other 16-lane row of the head
     return v;
 }
 
@@ -75,7 +88,9 @@ __device__ __forceinline__ float head_sum(float v)
 template <int L>
 __device__ __forceinline__ float half_head_partner(float v)
 {
-    if constexpr (L == 16)
+    if constexpr (L == 32)
+        return lane_xor16(v);
+    else if constexpr (L == 16)
         return dpp<0x128>(v);  // row_ror:8 == lane ^ 8 inside a 16-lane row
     else
         return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
@@ -410,7 +425,9 @@ KernelFn select_kernel(int head_dim, int style, int cos_layout, int cos_dtype, i
     const bool ph = cos_layout == QKR_COS_PER_HEAD;
     const bool cb = cos_dtype == QKR_BF16;
     const bool xf = dtype == QKR_FP16;
-    return head_dim == 128 ? select_s<128>(style, ph, cb, xf, l) : select_s<64>(style, ph, cb, xf, l);
+    if (head_dim == 128)
+        return select_s<128>(style, ph, cb, xf, l);
+    return head_dim == 64 ? select_s<64>(style, ph, cb, xf, l) : select_s<256>(style, ph, cb, xf, l);
 }
 
 int check_config(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype, int32_t style, int32_t dtype)
@@ -421,7 +438,7 @@ int check_config(int32_t head_dim, int32_t cos_layout, int32_t cos_dtype, int32_
         return QKR_ERR_ARG;
     if (cos_dtype < QKR_BF16 || cos_dtype > QKR_FP32 || dtype < QKR_BF16 || dtype > QKR_FP32)
         return QKR_ERR_ARG;
-    if (head_dim != 64 && head_dim != 128)
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
         return QKR_ERR_UNSUPPORTED;
     if (cos_dtype == QKR_FP16 || dtype == QKR_FP32)
         return QKR_ERR_UNSUPPORTED;
@@ -534,7 +551,7 @@ extern "C" const char* qknorm_rope_strerror(int status)
     case QKR_ERR_NULL: return "a required pointer is NULL";
     case QKR_ERR_SHAPE: return "a size is out of range or the sizes do not fit together";
     case QKR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case QKR_ERR_UNSUPPORTED: return "unsupported size or dtype (head_dim 64/128; hidden or spatial a multiple of 8)";
+    case QKR_ERR_UNSUPPORTED: return "unsupported size or dtype (head_dim 64/128/256; hidden or spatial a multiple of 8)";
     case QKR_ERR_MODE: return "pass either qkv, or q and/or k (not both, not neither)";
     case QKR_ERR_HIP: return "HIP launch or query failed";
     case QKR_ERR_ARG: return "eps not finite and > 0, an enum out of range, or a written buffer overlapping another";

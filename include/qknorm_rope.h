@@ -41,7 +41,7 @@ enum {
     QKR_ERR_NULL = -1,        /* a required pointer is NULL                          */
     QKR_ERR_SHAPE = -2,       /* tokens < 0, heads < 1, or a size over the limits    */
     QKR_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                    */
-    QKR_ERR_UNSUPPORTED = -4, /* head_dim not 64/128, or an unsupported dtype        */
+    QKR_ERR_UNSUPPORTED = -4, /* head_dim not 64/128/256, or an unsupported dtype    */
     QKR_ERR_MODE = -5,        /* not exactly one of {qkv} / {q and/or k}             */
     QKR_ERR_HIP = -6,         /* the kernel launch (or an attribute query) failed     */
     QKR_ERR_ARG = -7,         /* eps not finite and > 0, an enum out of range, or a   */
@@ -77,7 +77,7 @@ enum { QKR_ROPE_INTERLEAVED = 0, QKR_ROPE_ROTATE_HALF = 1 };
  * tokens      number of rows (batch folded in); 0 is a no-op that returns
  *             QKR_OK once the scalar arguments are valid (pointers unchecked).
  * heads       heads per tensor (Q, K and V have the same count), 1..65536.
- * head_dim    64 or 128.
+ * head_dim    64, 128 or 256.
  * q_gamma, k_gamma  fp32 [head_dim] norm weights.
  * eps         added to the mean square inside the root; finite and > 0.
  * cos, sin    cos_dtype (QKR_FP32 or QKR_BF16) tables, contiguous:

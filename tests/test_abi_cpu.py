@@ -55,7 +55,8 @@ def call(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(head_dim=96), b.QKR_ERR_UNSUPPORTED),
-    (dict(head_dim=256), b.QKR_ERR_UNSUPPORTED),
+    (dict(head_dim=512), b.QKR_ERR_UNSUPPORTED),
+    (dict(head_dim=32), b.QKR_ERR_UNSUPPORTED),
     (dict(dtype=b.QKR_FP32), b.QKR_ERR_UNSUPPORTED),
     (dict(cos_dtype=b.QKR_FP16), b.QKR_ERR_UNSUPPORTED),
     (dict(dtype=7), b.QKR_ERR_ARG),

@@ -76,9 +76,9 @@ def test_every_source_file_contributes_its_kernels(kernels):
     fams = {}
     for k in kernels:
         fams[_family(k[".name"])] = fams.get(_family(k[".name"]), 0) + 1
-    # 2 head dims x 2 styles x 2 table dtypes x 2 data dtypes x 2 block orders x
+    # 3 head dims x 2 styles x 2 table dtypes x 2 data dtypes x 2 block orders x
     # (4 unroll depths, shared layout + 3, per-head layout)
-    assert fams.get("qknorm_rope_kernel") == 224, fams
+    assert fams.get("qknorm_rope_kernel") == 336, fams
     # 8 row lengths x 2 data dtypes x 3 modulation dtypes x {1, 4} rows per
     # workgroup x {rows of exactly 512 * vectors per lane, other rows}
     assert fams.get("fuse_scale_shift_kernel") == 192, fams
@@ -102,7 +102,8 @@ def test_wave64_and_block_sizes(kernels):
         one_wave = "fuse_scale_shift_kernel" in k[".name"] and "Li1ELb" in k[".name"][-30:]
         assert k[".max_flat_workgroup_size"] == (64 if one_wave else 256), k[".name"]
         assert k[".agpr_count"] == 0, k[".name"]
-        assert k[".group_segment_fixed_size"] <= 4096, k[".name"]
+        # LDS: the largest is the staged cos/sin rows of 2 tokens at head_dim 256
+        assert k[".group_segment_fixed_size"] <= 8192, k[".name"]
 
 
 def waves_per_simd(vgprs: int) -> int:

@@ -131,7 +131,7 @@ def compare_fused(out, qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout="
 # ----------------------------------------------------------------------------- kernel resources
 
 
-@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
 @pytest.mark.parametrize("layout", ["shared", "per_head"])
 def test_kernels_do_not_spill(head_dim, layout):
     """Every instantiation (all unroll depths and block orders) has no scratch."""
@@ -139,7 +139,7 @@ def test_kernels_do_not_spill(head_dim, layout):
     for style in ("interleaved", "rotate_half"):
         for cd in (qkr.binding.QKR_FP32, qkr.binding.QKR_BF16):
             for xd in (qkr.binding.QKR_BF16, qkr.binding.QKR_FP16):
-                for heads in (1, 24, 40, 48, 72, 100):
+                for heads in (1, 10, 19, 24, 40, 48, 72, 100):
                     for tokens in (64, 100000):
                         info = qkr.kernel_info(head_dim, layout, cd, style, xd, heads=heads,
                                                tokens=tokens)
@@ -346,7 +346,8 @@ def test_byte_offsets_beyond_4gib():
     print("beyond 4 GiB max_abs", m)
 
 
-@pytest.mark.parametrize("heads,head_dim", [(3, 128), (24, 128), (48, 128), (72, 64), (100, 64)])
+@pytest.mark.parametrize("heads,head_dim", [(3, 128), (24, 128), (48, 128), (72, 64), (100, 64),
+                                            (30, 256)])
 def test_die_order_every_unroll(heads, head_dim):
     """8200 tokens = 4100 workgroups: the per-die token runs (with a ragged
     4100 % 8 remainder) for head counts that select each unroll depth."""
@@ -368,7 +369,7 @@ def test_die_order_every_unroll(heads, head_dim):
 
 
 @pytest.mark.parametrize("style", ["interleaved", "rotate_half"])
-@pytest.mark.parametrize("heads,head_dim", [(24, 64), (24, 128), (40, 128)])
+@pytest.mark.parametrize("heads,head_dim", [(24, 64), (24, 128), (40, 128), (16, 256)])
 def test_shared_row_matches_expanded_bitwise(style, heads, head_dim):
     """Shared fp32 row vs the same row materialised per head: rtol = atol = 0."""
     T = 256
@@ -414,7 +415,8 @@ def test_per_head_distinct_rows():
 
 
 @pytest.mark.parametrize("T,H,D", [(1, 1, 64), (1, 40, 128), (3, 5, 128), (5, 3, 64),
-                                   (257, 7, 128), (130, 33, 64), (2, 9, 128), (65, 17, 64)])
+                                   (257, 7, 128), (130, 33, 64), (2, 9, 128), (65, 17, 64),
+                                   (1, 1, 256), (67, 3, 256), (130, 25, 256)])
 @pytest.mark.parametrize("style", ["interleaved", "rotate_half"])
 def test_ragged_shapes(T, H, D, style):
     qkv = wl.fused_qkv(40 + T + H, T, H, D, "bf16")
@@ -639,11 +641,12 @@ def test_maximum_tokens():
 
 
 # heads giving each unroll depth (head iterations in flight), per head_dim
-SWEEP_HEADS = {128: {3: 5, 6: 20, 10: 40, 12: 48}, 64: {3: 9, 6: 44, 10: 72, 12: 100}}
+SWEEP_HEADS = {128: {3: 5, 6: 20, 10: 40, 12: 48}, 64: {3: 9, 6: 44, 10: 72, 12: 100},
+               256: {3: 5, 6: 11, 10: 19, 12: 30}}
 CODES = {"bf16": qkr.binding.QKR_BF16, "fp16": qkr.binding.QKR_FP16, "fp32": qkr.binding.QKR_FP32}
 
 
-@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
 @pytest.mark.parametrize("layout", ["shared", "per_head"])
 @pytest.mark.parametrize("table", ["fp32", "bf16"])
 @pytest.mark.parametrize("x_dtype", ["bf16", "fp16"])

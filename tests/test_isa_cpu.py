@@ -52,7 +52,7 @@ def disassembly(tmp_path_factory):
 
 def test_every_kernel_disassembled(disassembly):
     names = list(disassembly)
-    assert sum("qknorm_rope_kernel" in n for n in names) == 224
+    assert sum("qknorm_rope_kernel" in n for n in names) == 336
     assert sum("fuse_scale_shift_kernel" in n for n in names) == 192
     assert sum("gn_" in n for n in names) == 30
 
@@ -73,6 +73,6 @@ def test_bf16_outputs_use_the_packed_rne_convert(disassembly):
     # is the 5th argument; bf16 kernels must convert with v_cvt_pk_bf16_f32
     bf16 = [k for k in disassembly
             if re.search(r"qknorm_rope_kernelILi\d+ELi\dELb[01]ELb[01]ELb0E", k)]
-    assert len(bf16) == 112
+    assert len(bf16) == 168
     for k in bf16:
         assert any(i.startswith("v_cvt_pk_bf16_f32") for i in disassembly[k]), k
