@@ -78,6 +78,11 @@ WORKLOADS = {
         "large", 1005, "fused", 75600, 40, 128, ("bf16",),
         ("interleaved", "rotate_half"), ("shared", "per_head"), (21, 45, 80), (22, 21, 21),
         note="21x45x80 latent grid"),
+    # The headline's bytes with head_dim 256: 20 heads of 256 per tensor.
+    "wide_heads": Workload(
+        "wide_heads", 1008, "fused", 32760, 20, 256, ("bf16",), ("interleaved",),
+        ("shared", "per_head"), (21, 30, 52), (43, 43, 42),
+        note="Wan 21x30x52 grid, 20 heads of 256 (the headline's bytes at head_dim 256)"),
     # What one GPU of eight runs when the headline is sharded (the pass needs
     # no exchange): the last token shard, or one head shard of every token.
     "shard_tokens": Workload(
