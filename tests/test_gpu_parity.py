@@ -697,3 +697,59 @@ def test_every_kernel_instantiation(head_dim, layout, table, x_dtype):
                 assert_v_untouched(out, rows, H, D)
     assert hit == {(st, u, o) for st in ("interleaved", "rotate_half") for u in depths
                    for o in (0, 1)}, hit
+
+
+def _random_case(case, rng):
+    """One seeded draw from the whole call space of the pass (the tensor mode
+    cycles with the case number)."""
+    D = int(rng.choice([64, 128, 256]))
+    T = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(8190, 8400))]))
+    H = int(rng.integers(1, 1 + {64: 60, 128: 40, 256: 24}[D]))
+    return dict(
+        mode=("fused", "pair", "q", "k")[case % 4], D=D, T=T, H=min(H, 12) if T > 4000 else H,
+        style=str(rng.choice(["interleaved", "rotate_half"])),
+        layout=str(rng.choice(["shared", "per_head"])),
+        table=str(rng.choice(["fp32", "bf16"])), x_dtype=str(rng.choice(["bf16", "fp16"])))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_calls_across_the_api(case):
+    """24 seeded draws over tensor mode (fused, q and k, q alone, k alone),
+    head_dim, heads, tokens (small grids and grids past the per-die-runs
+    threshold), style, cos/sin layout and dtype and data dtype: every output
+    element against the oracle, tensors not passed bit-unchanged, canaries
+    intact."""
+    c = _random_case(case, np.random.default_rng(9000 + case))
+    T, H, D, style, layout = c["T"], c["H"], c["D"], c["style"], c["layout"]
+    xd = c["x_dtype"]
+    seed = 9100 + case
+    rows = T * (H if layout == "per_head" else 1)
+    cos, sin = tables(np.arange(rows) * 3 + 1, (D // 2,), D, style, dtype=c["table"])
+    if layout == "per_head":
+        cos, sin = cos.view(T, H, D), sin.view(T, H, D)
+    qg, kg = wl.norm_weights(seed, D)
+    what = "case %d %s" % (case, c)
+    if c["mode"] == "fused":
+        qkv = wl.fused_qkv(seed, T, H, D, xd)
+        out = run_fused(qkv, qg, kg, cos, sin, style, layout=layout)
+        compare_fused(out, qkv, xd, H, D, qg, kg, cos, sin, style, layout=layout, what=what)
+        return
+    q, k = wl.separate_qk(seed, T, H, D, (xd,))[xd]
+    qd, qbuf = guarded(q)
+    kd, kbuf = guarded(k)
+    args = dict(cos=dev(cos), sin=dev(sin), style=style, cos_layout=layout)
+    if c["mode"] in ("pair", "q"):
+        args.update(q=qd, q_gamma=dev(qg))
+    if c["mode"] in ("pair", "k"):
+        args.update(k=kd, k_gamma=dev(kg))
+    qkr.qknorm_rope_fused(**args)
+    torch.cuda.synchronize()
+    assert canaries_intact(qbuf) and canaries_intact(kbuf), what
+    kw = dict(row_stride=H * D, col0=0, heads=H, head_dim=D, eps=wl.EPS, cos=table_np(cos),
+              sin=table_np(sin), cos_dtype=c["table"], cos_layout=layout, style=style)
+    for name, t_in, t_dev, g in (("q", q, qd, qg), ("k", k, kd, kg)):
+        if c["mode"] in (name, "pair"):
+            ref = oracle.qknorm_rope(wl.u16(t_in), xd, gamma=g.numpy(), **kw)
+            check_close(_decode(t_dev, xd), ref, xd, what + " " + name)
+        else:
+            assert torch.equal(t_dev.cpu().view(torch.int16), t_in.view(torch.int16)), what
