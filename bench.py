@@ -17,6 +17,7 @@ oracle on a bounded sample of the same workload.
                   [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
   python bench.py --op group_norm_silu [--workload gn_vae_out|gn_vae_up|gn_vae_mid]
                   [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
+  python bench.py --op eager_chain [--workload flux|headline|mid] [--dtype bf16|fp16]
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                   [--layout shared|per_head] [--style interleaved|rotate_half]
                   [--dtype bf16|fp16] [--flush] [--graph] [--no-cpu-baseline] [--calib-copy]
@@ -93,7 +94,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="qknorm_rope",
-                    choices=["qknorm_rope", "fuse_scale_shift", "group_norm_silu"])
+                    choices=["qknorm_rope", "fuse_scale_shift", "group_norm_silu",
+                             "eager_chain"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mod-dtype", default="fp32", choices=["fp32", "bf16", "fp16"])
     ap.add_argument("--inplace", action="store_true", help="AdaLN, group norm: write y over x")
@@ -455,6 +457,118 @@ def bench_group_norm_silu(args):
     return 0
 
 
+def eager_chain(x, gamma, cos, sin, eps, style):
+    """The unfused form of the pass on one tensor in PyTorch eager mode, as a
+    DiT block runs it without a fused kernel ([FLUX PR], intro: a chain of
+    per-head RMSNorms and RoPEs; its microbench compares against PyTorch
+    eager bf16).  A comparison leg for timing only, never the product path.
+
+    x [T, H, D] (any strides) in bf16/fp16; gamma [D] in x's dtype, as a
+    norm module's weight; cos, sin [T, D] fp32.  The norm's output is
+    rounded to x's dtype, then RoPE runs on that rounded tensor in fp32 and
+    rounds again.  Returns a new [T, H, D] tensor; x is not modified."""
+    import torch
+    import torch.nn.functional as F
+    D = x.shape[-1]
+    n = F.rms_norm(x, (D,), weight=gamma, eps=eps)
+    if style == "interleaved":              # partner of 2i is 2i+1, with the sign of the sine
+        pairs = n.unflatten(-1, (D // 2, 2))
+        rot = torch.stack((-pairs[..., 1], pairs[..., 0]), dim=-1).flatten(-2)
+    else:                                   # partner of i is i + D/2
+        rot = torch.cat((-n[..., D // 2:], n[..., :D // 2]), dim=-1)
+    c, s = cos.unsqueeze(1), sin.unsqueeze(1)
+    return (n.float() * c + rot.float() * s).to(x.dtype)
+
+
+def bench_eager_chain(args):
+    """Fused pass vs the eager unfused chain on the same tensors and stream,
+    the form of the [FLUX PR] kernel microbench.  On the FLUX workload the
+    shapes are its text stream (512 tokens), image stream (4096) and the
+    joint sequence (4608), 48 heads of 128; other workloads run whole.
+    Prints one JSON line; `value` is the speedup on the last (largest) shape."""
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_qk_amd as qkr
+    import workloads as wl
+    w = wl.WORKLOADS[args.workload or "flux"]
+    style = args.style or w.styles[0]
+    dtype = args.dtype or "bf16"
+    H, D, T = w.heads, w.head_dim, w.tokens
+    dev = torch.device("cuda:0")
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, style)
+    c, s = cos.to(dev), sin.to(dev)
+    g1, g2 = qg.to(dev), kg.to(dev)
+    # the norm module's weight lives in the data dtype; the fused call gets
+    # the same values widened to fp32, so both compute the same function
+    tdt = wl.DTYPES[dtype]
+    g1e, g2e = g1.to(tdt), g2.to(tdt)
+    g1f, g2f = g1e.float(), g2e.float()
+    if w.layout == "fused":
+        qkv = wl.fused_qkv(w.seed, T, H, D, dtype).to(dev)
+        q_all = qkv[:, :H * D].view(T, H, D)
+        k_all = qkv[:, H * D:2 * H * D].view(T, H, D)
+    else:
+        q_cpu, k_cpu = wl.separate_qk(w.seed, T, H, D, (dtype,))[dtype]
+        q_all, k_all = q_cpu.to(dev), k_cpu.to(dev)
+    if w.key == "flux":
+        spans = [("text stream", 0, w.text_tokens), ("image stream", w.text_tokens, T),
+                 ("joint sequence", 0, T)]
+    else:
+        spans = [(w.key, 0, T)]
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+    shapes = []
+    for name, a, b in spans:
+        # contiguous copies of the token range, so that both sides read the
+        # same dense [tokens, H, D] tensors (fused mode keeps its row stride)
+        if w.layout == "fused":
+            buf = qkv[a:b].clone()
+            q, k = buf[:, :H * D].view(b - a, H, D), buf[:, H * D:2 * H * D].view(b - a, H, D)
+            tensors = dict(qkv=buf)
+        else:
+            q, k = q_all[a:b].clone(), k_all[a:b].clone()
+            tensors = dict(q=q, k=k)
+        cs, ss = c[a:b].contiguous(), s[a:b].contiguous()
+        q0, k0 = q.clone(), k.clone()
+
+        def eager():
+            with torch.cuda.stream(stream):
+                eager_chain(q0, g1e, cs, ss, wl.EPS, style)
+                eager_chain(k0, g2e, cs, ss, wl.EPS, style)
+
+        def fused():
+            qkr.qknorm_rope_fused(**tensors, q_gamma=g1f, k_gamma=g2f, cos=cs, sin=ss,
+                                  eps=wl.EPS, style=style, stream=handle)
+
+        per_e, _, _ = time_launches(eager, stream, args.steps, args.warmup)
+        per_f, _, _ = time_launches(fused, stream, args.steps, args.warmup)
+        nbytes = wl.algorithmic_bytes(b - a, H, D)
+        fe, ff = float(per_e.mean()), float(per_f.mean())
+        shapes.append({"shape": "%s [%d, %d, %d] x {q, k}" % (name, b - a, H, D),
+                       "tokens": b - a, "eager_us": round(fe, 2), "fused_us": round(ff, 2),
+                       "speedup": round(fe / ff, 2),
+                       "fused_pct_of_peak": round(100 * nbytes / (ff * 1e-6) / 1e9 / PEAK_GBS, 2)})
+    last = shapes[-1]
+    result = {
+        "metric": "fused QK-norm+RoPE speedup over the PyTorch eager unfused chain",
+        "value": last["speedup"], "unit": "x", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "%s: %s %s, %d heads x %d, %s RoPE, shared fp32 cos/sin; eager: "
+                               "F.rms_norm -> round -> RoPE -> round per tensor, warm caches"
+                               % (w.key, "fused QKV" if w.layout == "fused" else "separate q, k",
+                                  dtype, H, D, style),
+                   "data_dtype": dtype, "parallelism": "single GPU"},
+        "shapes": shapes,
+        "context": "[FLUX PR] reports 15.8x-25.7x over PyTorch eager bf16 across FLUX.2 shapes "
+                   "on another machine",
+    }
+    print(json.dumps(result))
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -476,6 +590,8 @@ def main():
         return bench_fuse_scale_shift(args)
     if args.op == "group_norm_silu":
         return bench_group_norm_silu(args)
+    if args.op == "eager_chain":
+        return bench_eager_chain(args)
     args.workload = args.workload or "headline"
     w = wl.WORKLOADS[args.workload]
     style = args.style or w.styles[0]
