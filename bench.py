@@ -572,7 +572,7 @@ def bench_eager_chain(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the pass needs no collective; "
+        print("bench.py: measures one GPU only (the pass needs no collective; "
               "run with --gpus 1)", file=sys.stderr)
         return 2
     import numpy as np

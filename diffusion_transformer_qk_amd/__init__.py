@@ -8,11 +8,13 @@ The passes run in hand-written HIP kernels behind the C ABI of
 """
 from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, QkrError, dit_fuse_scale_shift_raw, dit_group_norm_silu_raw,
-    fuse_scale_shift, group_norm_silu, group_norm_silu_workspace_size, kernel_info,
+    fuse_scale_shift, group_norm_silu, group_norm_silu_schedule,
+    group_norm_silu_workspace_size, kernel_info,
     load_library, qknorm_rope_fused, qknorm_rope_fused_raw, strerror, version,
 )
 
 __all__ = ["qknorm_rope_fused", "qknorm_rope_fused_raw", "fuse_scale_shift",
-           "dit_fuse_scale_shift_raw", "group_norm_silu", "group_norm_silu_workspace_size",
+           "dit_fuse_scale_shift_raw", "group_norm_silu", "group_norm_silu_schedule",
+           "group_norm_silu_workspace_size",
            "dit_group_norm_silu_raw", "kernel_info", "load_library", "strerror", "version",
            "QkrError", "EXPORTS", "LIB_PATH"]

@@ -31,7 +31,8 @@ STYLES = {"interleaved": QKR_ROPE_INTERLEAVED, "rotate_half": QKR_ROPE_ROTATE_HA
 TENSORS = {"fused": QKR_TENSORS_FUSED, "pair": QKR_TENSORS_PAIR, "one": QKR_TENSORS_ONE}
 EXPORTS = ("qknorm_rope_fused", "qknorm_rope_strerror", "qknorm_rope_version",
            "qknorm_rope_kernel_info", "dit_fuse_scale_shift",
-           "dit_group_norm_silu_workspace_size", "dit_group_norm_silu")
+           "dit_group_norm_silu_workspace_size", "dit_group_norm_silu_schedule",
+           "dit_group_norm_silu")
 MOD_DTYPES = {"bf16": QKR_BF16, "fp16": QKR_FP16, "fp32": QKR_FP32}
 
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.dit_fuse_scale_shift.restype = ctypes.c_int
     lib.dit_group_norm_silu_workspace_size.argtypes = [i64, i32, i64, i32]
     lib.dit_group_norm_silu_workspace_size.restype = i64
+    lib.dit_group_norm_silu_schedule.argtypes = [i64, i32, i64, i32, ctypes.POINTER(i64)]
+    lib.dit_group_norm_silu_schedule.restype = i32
     lib.dit_group_norm_silu.argtypes = [vp, vp, i64, i32, i64, i32, vp, vp, i32, f32, i32, vp, i64,
                                         vp]
     lib.dit_group_norm_silu.restype = ctypes.c_int
@@ -297,6 +300,20 @@ def fuse_scale_shift(x, scale, shift, *, out=None, eps: float = 1e-6,
 def group_norm_silu_workspace_size(n: int, channels: int, spatial: int, groups: int) -> int:
     """Workspace bytes the call needs (negative: a QKR_ERR_* code for bad sizes)."""
     return int(load_library().dit_group_norm_silu_workspace_size(n, channels, spatial, groups))
+
+
+GN_SCHEDULES = {0: "one_read", 1: "lagged", 2: "two_pass"}
+
+
+def group_norm_silu_schedule(n: int, channels: int, spatial: int, groups: int):
+    """(schedule name, elements per chunk) the library would use for these
+    sizes: "one_read", "lagged" or "two_pass" (see include/group_norm_silu.h)."""
+    chunk = ctypes.c_int64(0)
+    code = int(load_library().dit_group_norm_silu_schedule(n, channels, spatial, groups,
+                                                           ctypes.byref(chunk)))
+    if code < 0:
+        raise QkrError(code, strerror(code))
+    return GN_SCHEDULES[code], int(chunk.value)
 
 
 def dit_group_norm_silu_raw(x: int, y: int, n: int, channels: int, spatial: int, groups: int,

@@ -9,15 +9,22 @@
 //   * one chunk per group: a single kernel keeps the chunk in registers,
 //     reduces mean and biased variance in two passes and writes y (one read,
 //     one write);
-//   * several chunks: gn_stats_kernel reduces each chunk to (mean, sum of
-//     squared deviations) in the workspace, then gn_apply_kernel combines
-//     the group's partials with the pairwise update (sum n_i m_i / N, then
-//     sum M2_i + n_i (m_i - m)^2) in a fixed order, so every workgroup of a
-//     group gets the same statistics, re-reads its chunk and writes y.  One
-//     launch of each covers every group (measured faster than slabs of
-//     48-192 MB, whose extra launches cost more than the Infinity Cache
-//     returns): the stats pass reads with ordinary loads, the apply pass
-//     re-reads with non-temporal loads and writes non-temporally.
+//   * several chunks, large calls (gn_lagged_kernel): workgroup b reduces
+//     chunk b to (mean, sum of squared deviations) and publishes it as one
+//     64-bit word, then writes the output of chunk b - lag.  It waits until
+//     every word of that chunk's group is published (all belong to lower
+//     workgroups; one still missing after a short wait is reduced by the
+//     waiter itself), combines them and re-reads the chunk.  Workgroups are
+//     dealt to the dies in turn and lag is a multiple of 8, so the re-read
+//     runs on the die that read the chunk a few MB earlier and comes from its
+//     L2: HBM sees x once;
+//   * several chunks, small calls: gn_stats_kernel writes every chunk's
+//     partial statistics to the workspace, then gn_apply_kernel re-reads
+//     each chunk (two launches; x is read twice).
+//   Both combine a group's partials with the pairwise update (sum n_i m_i / N,
+//   then sum M2_i + n_i (m_i - m)^2) in the same fixed order, so every
+//   workgroup of a group gets the same statistics and both schedules give
+//   identical bits.
 // Per vector of 8 elements (spatial is a multiple of 8, so a vector never
 // straddles channels): t = fma(x - mean, rstd * gamma[c], beta[c]),
 // y = t * rcp(1 + exp(-t)), packed with round-to-nearest-even.
@@ -25,6 +32,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "device_common.h"
 #include "host_common.h"
@@ -57,6 +65,9 @@ struct GnParams {
     int32_t groups;
     int32_t chunks;          // chunks per group
     float eps;
+    int64_t total;           // chunks of the call (pairs * chunks)
+    int64_t lag;             // lagged schedule: chunks between a reduction and an output
+    int32_t wait_polls;      // lagged schedule: polls of a word before reducing it here
 };
 
 // Vectors valid in chunk k of a group.
@@ -123,6 +134,42 @@ __device__ __forceinline__ void chunk_moments(u32x4 (&v)[VPT], int nv, float* re
     }
     m2 = block_sum<kWaves>(ss, red1);
     forget_unpacked(v);
+}
+
+// chunk_moments over a chunk read from memory one vector at a time (the same
+// vectors, sums and order, so the same bits), for callers that cannot spare
+// registers for the whole chunk.
+template <bool X_FP16, int VPT>
+__device__ __forceinline__ void chunk_moments_streamed(const uint16_t* base, int nv, float* red0,
+                                                       float* red1, float& mean, float& m2)
+{
+    float sum = 0.0f;
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        const u32x4 t = load16<false>(base + (int64_t)(i < nv ? i : nv - 1) * kVec);
+        float f[8];
+        unpack8<X_FP16>(i < nv ? t : u32x4{0, 0, 0, 0}, f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            sum += f[k];
+    }
+    mean = block_sum<kWaves>(sum, red0) / (float)(nv * kVec);
+    float ss = 0.0f;
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        if (i < nv) {
+            float f[8];
+            unpack8<X_FP16>(load16<false>(base + (int64_t)i * kVec), f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float d = f[k] - mean;
+                ss = __builtin_fmaf(d, d, ss);
+            }
+        }
+    }
+    m2 = block_sum<kWaves>(ss, red1);
 }
 
 template <int PARAM>
@@ -229,36 +276,27 @@ __global__ __launch_bounds__(kBlock) void gn_stats_kernel(const GnParams p)
     }
 }
 
-// Several chunks, pass 2: combine the group's partials, write the chunk.
-template <bool X_FP16, int PARAM, int VPT>
-__global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
+// Group mean and 1/sqrt(var + eps) from the group's chunk partials `part`
+// ([chunks][2]), given this thread's first partial `first` (of chunk
+// threadIdx.x, if there is one).  Same order in every workgroup of the group:
+// thread sums over i = tid, tid + 256, ..., then the fixed-order workgroup
+// reduction through red0 and red1.
+template <int VPT>
+__device__ __forceinline__ void combine_partials(const GnParams& p, const float* part,
+                                                 f32x2 first, float* red0, float* red1,
+                                                 float& mean, float& rstd)
 {
     constexpr int64_t kChunk = chunk_elems<VPT>();
-    __shared__ float red[2][kWaves];
-    const int64_t q = blockIdx.x / p.chunks;
-    const int k = (int)(blockIdx.x % p.chunks);
-    const int nv = chunk_vectors<VPT>(p, k);
-    const float* part = p.partial + 2 * q * p.chunks;
     const float last_n = (float)(p.group_size - (int64_t)(p.chunks - 1) * kChunk);
-    // This thread's first partial is read before the chunk, so that the
-    // combine (two workgroup reductions) runs while the chunk is in flight.
     const int i0 = threadIdx.x;
     const bool has0 = i0 < p.chunks;
-    f32x2 first = {0.0f, 0.0f};
-    if (has0)
-        first = *reinterpret_cast<const f32x2*>(part + 2 * i0);
-    u32x4 v[VPT];
-    load_chunk<true>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
-
-    // Same order in every workgroup of the group: thread sums over
-    // i = tid, tid + 256, ..., then the fixed-order workgroup reduction.
     const float n0 = i0 == p.chunks - 1 ? last_n : (float)kChunk;
     float s = has0 ? n0 * first[0] : 0.0f;
     for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
         const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
         s = __builtin_fmaf(n_i, part[2 * i], s);
     }
-    const float mean = block_sum<kWaves>(s, red[0]) / (float)p.group_size;
+    mean = block_sum<kWaves>(s, red0) / (float)p.group_size;
     float m2 = 0.0f;
     if (has0) {
         const float d = first[0] - mean;
@@ -269,9 +307,156 @@ __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
         const float d = part[2 * i] - mean;
         m2 += __builtin_fmaf(n_i * d, d, part[2 * i + 1]);
     }
-    const float rstd = __builtin_amdgcn_rsqf(block_sum<kWaves>(m2, red[1]) / (float)p.group_size
-                                             + p.eps);
+    rstd = __builtin_amdgcn_rsqf(block_sum<kWaves>(m2, red1) / (float)p.group_size + p.eps);
+}
+
+// Several chunks, pass 2: combine the group's partials, write the chunk.
+template <bool X_FP16, int PARAM, int VPT>
+__global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
+{
+    constexpr int64_t kChunk = chunk_elems<VPT>();
+    __shared__ float red[2][kWaves];
+    const int64_t q = blockIdx.x / p.chunks;
+    const int k = (int)(blockIdx.x % p.chunks);
+    const int nv = chunk_vectors<VPT>(p, k);
+    const float* part = p.partial + 2 * q * p.chunks;
+    // This thread's first partial is read before the chunk, so that the
+    // combine (two workgroup reductions) runs while the chunk is in flight.
+    f32x2 first = {0.0f, 0.0f};
+    if ((int)threadIdx.x < p.chunks)
+        first = *reinterpret_cast<const f32x2*>(part + 2 * threadIdx.x);
+    u32x4 v[VPT];
+    load_chunk<true>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
+    float mean, rstd;
+    combine_partials<VPT>(p, part, first, red[0], red[1], mean, rstd);
     chunk_apply<X_FP16, PARAM>(p, q, k, nv, v, mean, rstd);
+}
+
+// Lagged schedule.  A chunk's word in the workspace holds its mean (low 32
+// bits) and sum of squared deviations (high 32 bits), the layout of the
+// two-pass partials; kEmpty (two all-ones NaNs, which no reduction of 16-bit
+// data produces) marks a word not yet published.
+constexpr uint64_t kEmpty = ~0ull;
+// Polls of an unpublished word (a few ms) before a workgroup reduces that
+// chunk itself.  Never reached in a lone call, where the chunks an output
+// waits for were reduced several hundred workgroups earlier.  The environment
+// variable QKR_GN_WAIT_POLLS overrides it (0: reduce at once), which makes
+// every waiter take the reduce-it-here path.
+constexpr int kWaitPolls = 1 << 12;
+
+// Mark every chunk word of the call as not yet published.
+__global__ __launch_bounds__(kBlock) void gn_clear_kernel(const GnParams p)
+{
+    uint64_t* word = reinterpret_cast<uint64_t*>(p.partial);
+    for (int64_t i = blockIdx.x * (int64_t)kBlock + threadIdx.x; i < p.total;
+         i += (int64_t)gridDim.x * kBlock)
+        word[i] = kEmpty;
+}
+
+// Reduce chunk k of group q and publish its word if none is published yet.
+// The first word published for a chunk stands (compare-and-swap from
+// kEmpty): every workgroup of the group then combines the same statistics,
+// and in place, a reduction that read data the chunk's output had already
+// replaced never stands, since that output was written only after a word
+// was published.  Returns, in thread 0, the word that stands.
+template <bool X_FP16, bool STREAMED>
+__device__ __forceinline__ uint64_t reduce_and_publish(const GnParams& p, int64_t q, int k,
+                                                       float* red0, float* red1)
+{
+    constexpr int VPT = kVptMax;
+    const int nv = chunk_vectors<VPT>(p, k);
+    const uint16_t* const base = p.x + q * p.group_size + (int64_t)k * chunk_elems<VPT>();
+    float mean, m2;
+    if constexpr (STREAMED) {
+        chunk_moments_streamed<X_FP16, VPT>(base, nv, red0, red1, mean, m2);
+    } else {
+        u32x4 v[VPT];
+        load_chunk<false>(base, nv, v);
+        chunk_moments<X_FP16>(v, nv, red0, red1, mean, m2);
+    }
+    uint64_t stands = 0;
+    if (threadIdx.x == 0) {
+        uint64_t* const w = reinterpret_cast<uint64_t*>(p.partial) + q * p.chunks + k;
+        const uint64_t mine = (uint64_t)__float_as_uint(mean) | ((uint64_t)__float_as_uint(m2) << 32);
+        uint64_t expected = kEmpty;
+        stands = __hip_atomic_compare_exchange_strong(w, &expected, mine, __ATOMIC_RELAXED,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     ? mine : expected;
+    }
+    return stands;
+}
+
+// Workgroup b: statistics of chunk b (b < total), then the output of chunk
+// j = b - lag (0 <= j < total).  lag >= chunks, so every chunk of j's group
+// belongs to a lower workgroup, normally finished long before.  A word still
+// unpublished after p.wait_polls polls (its workgroup has not run yet: other
+// work may hold the die) is reduced here instead, so every workgroup ends
+// whatever order the workgroups start in.
+template <bool X_FP16, int PARAM>
+__global__ __launch_bounds__(kBlock) void gn_lagged_kernel(const GnParams p)
+{
+    constexpr int VPT = kVptMax;
+    constexpr int64_t kChunk = chunk_elems<VPT>();
+    __shared__ float red[4][kWaves];
+    __shared__ int missing;
+    __shared__ uint64_t helped;
+    const int64_t b = blockIdx.x;
+    const int64_t j = b - p.lag;
+    const bool out = j >= 0 && j < p.total;
+    int64_t qo = 0;
+    int ko = 0, nvo = 0;
+    u32x4 w[VPT];
+    if (out) {      // the output chunk's loads depend on nothing: issue them first
+        qo = j / p.chunks;
+        ko = (int)(j % p.chunks);
+        nvo = chunk_vectors<VPT>(p, ko);
+        load_chunk<true>(p.x + qo * p.group_size + (int64_t)ko * kChunk, nvo, w);
+    }
+    if (b < p.total)
+        reduce_and_publish<X_FP16, false>(p, b / p.chunks, (int)(b % p.chunks), red[0], red[1]);
+    if (!out)
+        return;
+
+    // chunks <= 256: thread i watches the word of chunk i of the output's group
+    const int i = threadIdx.x;
+    const bool watch = i < p.chunks;
+    uint64_t* const grp = reinterpret_cast<uint64_t*>(p.partial) + qo * p.chunks;
+    uint64_t bits = 0;
+    if (watch) {
+        bits = __hip_atomic_load(grp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int spin = 0; bits == kEmpty && spin < p.wait_polls; ++spin) {
+            __builtin_amdgcn_s_sleep(1);
+            bits = __hip_atomic_load(grp + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (__syncthreads_or(watch && bits == kEmpty)) {
+        // Rare: reduce the chunks still unpublished here, lowest first, one
+        // vector at a time (the output chunk stays loaded in registers).
+        for (;;) {
+            if (i == 0)
+                missing = kBlock;
+            __syncthreads();
+            if (watch && bits == kEmpty)
+                atomicMin(&missing, i);
+            __syncthreads();
+            const int m = missing;
+            if (m == kBlock)
+                break;
+            const uint64_t stands = reduce_and_publish<X_FP16, true>(p, qo, m, red[0], red[1]);
+            if (i == 0)
+                helped = stands;
+            __syncthreads();
+            if (i == m)
+                bits = helped;
+            __syncthreads();        // every thread has read `missing` and `helped`
+        }
+    }
+    const f32x2 first = watch ? f32x2{__uint_as_float((uint32_t)bits),
+                                      __uint_as_float((uint32_t)(bits >> 32))}
+                              : f32x2{0.0f, 0.0f};
+    float mean, rstd;
+    combine_partials<VPT>(p, p.partial + 2 * qo * p.chunks, first, red[2], red[3], mean, rstd);
+    chunk_apply<X_FP16, PARAM>(p, qo, ko, nvo, w, mean, rstd);
 }
 
 using GnFn = void (*)(GnParams);
@@ -288,6 +473,13 @@ GnFn pick_apply(int prm)
 {
     return prm == QKR_FP32 ? gn_apply_kernel<XF, QKR_FP32, VPT>
          : prm == QKR_FP16 ? gn_apply_kernel<XF, QKR_FP16, VPT> : gn_apply_kernel<XF, QKR_BF16, VPT>;
+}
+
+template <bool XF>
+GnFn pick_lagged(int prm)
+{
+    return prm == QKR_FP32 ? gn_lagged_kernel<XF, QKR_FP32>
+         : prm == QKR_FP16 ? gn_lagged_kernel<XF, QKR_FP16> : gn_lagged_kernel<XF, QKR_BF16>;
 }
 
 template <int VPT>
@@ -313,6 +505,32 @@ int launch(GnFn fn, int64_t blocks, const GnParams& p, hipStream_t stream)
 constexpr int64_t kFillBlocks = 2048;
 // A launch grid holds fewer than 2^32 work-items.
 constexpr int64_t kMaxBlocks = 0xFFFFFFFFll / kBlock;
+// The lagged schedule: used from this many 16K-element chunks per call (below
+// it the two launches are as fast: the whole input stays in the Infinity
+// Cache), for groups of at most one chunk per thread of a workgroup.  Its
+// lag is the group's chunks plus kLagExtra, rounded up to a multiple of the
+// dies, so that a chunk is re-read about 3 MB later on the die that read it.
+constexpr int64_t kLaggedFromChunks = 4096;
+constexpr int kLaggedMaxChunks = kBlock;
+constexpr int64_t kLagExtra = 512;
+
+enum Schedule { kOneRead = 0, kLagged = 1, kTwoPass = 2 };
+
+// How a call of this shape runs (chunks and vpt from check_shape).
+Schedule schedule_for(int64_t pairs, int64_t chunks, int vpt, int64_t* lag)
+{
+    *lag = 0;
+    if (chunks == 1)
+        return kOneRead;
+    const int64_t total = pairs * chunks;
+    const int64_t l = (chunks + kLagExtra + kXcds - 1) / kXcds * kXcds;
+    if (vpt == kVptMax && chunks <= kLaggedMaxChunks && total >= kLaggedFromChunks &&
+        total + l <= kMaxBlocks) {
+        *lag = l;
+        return kLagged;
+    }
+    return kTwoPass;
+}
 
 // Shape checks shared by the size query and the call.  Sets pairs (samples x
 // groups), the vectors per thread of a chunk (8, 4 or 2: the largest that
@@ -358,6 +576,19 @@ extern "C" int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channel
     if (rc != QKR_OK)
         return rc;
     return chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
+}
+
+extern "C" int32_t dit_group_norm_silu_schedule(int64_t n, int32_t channels, int64_t spatial,
+                                                int32_t groups, int64_t* chunk_elems_out)
+{
+    int64_t chunks = 0, pairs = 0, lag = 0;
+    int vpt = 0;
+    const int rc = check_shape(n, channels, spatial, groups, &chunks, &pairs, &vpt);
+    if (rc != QKR_OK)
+        return rc;
+    if (chunk_elems_out)
+        *chunk_elems_out = (int64_t)kBlock * vpt * kVec;
+    return schedule_for(pairs, chunks, vpt, &lag);
 }
 
 extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels,
@@ -410,12 +641,27 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
     p.groups = groups;
     p.chunks = (int32_t)chunks;
     p.eps = eps;
+    p.total = pairs * chunks;
+    p.wait_polls = kWaitPolls;
+    if (const char* env = getenv("QKR_GN_WAIT_POLLS")) {
+        const long v = strtol(env, nullptr, 10);
+        p.wait_polls = v < 0 ? 0 : v > kWaitPolls ? kWaitPolls : (int32_t)v;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool xf = dtype == QKR_FP16;
 
-    if (chunks == 1)
+    const Schedule sched = schedule_for(pairs, chunks, vpt, &p.lag);
+    if (sched == kOneRead)
         return launch(xf ? pick_single<true>(param_dtype) : pick_single<false>(param_dtype), pairs,
                       p, s);
+    if (sched == kLagged) {
+        const int64_t clear_blocks = (p.total + kBlock - 1) / kBlock;
+        const int r = launch(gn_clear_kernel, clear_blocks < 1024 ? clear_blocks : 1024, p, s);
+        return r == QKR_OK ? launch(xf ? pick_lagged<true>(param_dtype)
+                                       : pick_lagged<false>(param_dtype),
+                                    p.total + p.lag, p, s)
+                           : r;
+    }
 
     GnFn stats, apply;
     if (vpt == 8)

@@ -19,7 +19,9 @@
  * Math is fp32; y is rounded once, to nearest even, to x's dtype.  Large
  * groups are reduced in chunks whose partial statistics (mean and sum of
  * squared deviations per chunk) go to a caller-owned workspace; the chunks
- * are then combined exactly as a two-level reduction (Chan et al.).
+ * are then combined exactly as a two-level reduction (Chan et al.).  Every
+ * schedule combines them in the same order, so a shape's output bits do not
+ * depend on which schedule runs it (dit_group_norm_silu_schedule).
  *
  * Pointers are DEVICE pointers owned by the caller; the library allocates,
  * frees and synchronises nothing.  y may be x itself or a buffer that does
@@ -43,6 +45,31 @@ extern "C" {
  */
 int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channels, int64_t spatial,
                                            int32_t groups);
+
+/*
+ * dit_group_norm_silu_schedule -- how dit_group_norm_silu runs a call with
+ * these sizes, or a negative QKR_ERR_* code for sizes it would reject.  If
+ * chunk_elems is not NULL it receives the elements per chunk (16384, 8192 or
+ * 4096; a group of one chunk may be shorter).  Returns
+ *   0  one chunk per group: one kernel reads each group once;
+ *   1  lagged single read: one kernel in which workgroup b publishes chunk
+ *      b's statistics to the workspace and then writes chunk b - lag, after
+ *      waiting for every chunk of that chunk's group (all held by lower
+ *      workgroups); x comes from HBM once, the second read of a chunk from
+ *      the L2 of the die that first read it.  Taken from 4096 chunks of 16384
+ *      elements per call, for groups of at most 256 chunks.  A workgroup
+ *      that finds a word still unpublished after a few ms of polling reduces
+ *      that chunk itself; the first word published for a chunk stands
+ *      (compare-and-swap), so the call ends whatever order its workgroups
+ *      start in, also beside other work.  The environment variable
+ *      QKR_GN_WAIT_POLLS (read per call; default and maximum 4096) sets the
+ *      polls before that; 0 makes every waiter reduce at once, which tests
+ *      use to exercise that path.  A small kernel first marks the
+ *      workspace's words unpublished;
+ *   2  two passes: a statistics kernel, then an apply kernel that re-reads x.
+ */
+int32_t dit_group_norm_silu_schedule(int64_t n, int32_t channels, int64_t spatial, int32_t groups,
+                                     int64_t* chunk_elems);
 
 /*
  * dit_group_norm_silu -- group norm + SiLU of an [n, channels, spatial] tensor.

@@ -66,6 +66,17 @@ int main(void)
         printf("FAIL workspace size\n");
         return 1;
     }
+    {
+        int64_t chunk = 0;
+        EXPECT(dit_group_norm_silu_schedule(1, 512, 128 * 128, 32, &chunk), 2);
+        if (chunk != 4096) {
+            printf("FAIL schedule chunk %lld\n", (long long)chunk);
+            return 1;
+        }
+        EXPECT(dit_group_norm_silu_schedule(1, 128, 1024 * 1024, 32, NULL), 1);
+        EXPECT(dit_group_norm_silu_schedule(2, 64, 512, 32, NULL), 0);
+        EXPECT(dit_group_norm_silu_schedule(1, 30, 64, 4, NULL), QKR_ERR_SHAPE);
+    }
     EXPECT(dit_group_norm_silu(a, b, 1, 512, 128 * 128, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16, NULL,
                                0, NULL), QKR_ERR_ARG);          /* y inside x's 16 MB */
     EXPECT(dit_group_norm_silu(a, far, 1, 512, 128 * 128, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16,

@@ -25,7 +25,7 @@ def declared_functions():
         if h.endswith(".h"):
             with open(os.path.join(INCLUDE, h)) as f:
                 text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-            names |= set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(\w+)\s*\(", text,
+            names |= set(re.findall(r"^\s*(?:int|int32_t|int64_t|const char\*)\s+(\w+)\s*\(", text,
                                     flags=re.M))
     return names
 
@@ -281,3 +281,26 @@ def test_group_norm_rejects_before_any_hip_call(over, code):
 
 def test_group_norm_zero_samples_is_a_no_op():
     assert gn(n=0, x=0, y=0, gamma=0, beta=0) == b.QKR_OK
+
+
+@pytest.mark.parametrize("n,channels,spatial,groups,want", [
+    (2, 64, 512, 32, ("one_read", 16384)),             # a group fits one chunk
+    (1, 128, 1024 * 1024, 32, ("lagged", 16384)),      # VAE out: 8,192 chunks of 256 per group
+    (1, 256, 512 * 512, 32, ("lagged", 16384)),        # VAE up: 4,096 chunks
+    (8, 512, 16384, 32, ("lagged", 16384)),            # exactly 4,096 chunks
+    (4, 512, 16384, 32, ("two_pass", 16384)),          # 2,048 chunks: below the lagged threshold
+    (1, 512, 128 * 128, 32, ("two_pass", 4096)),       # VAE mid: small chunks fill the chip
+    (1, 64, 2048 * 2048, 32, ("two_pass", 16384)),     # 512 chunks per group: over 256
+])
+def test_group_norm_schedule_by_shape(n, channels, spatial, groups, want):
+    assert qkr.group_norm_silu_schedule(n, channels, spatial, groups) == want
+
+
+def test_group_norm_schedule_rejects_what_the_call_rejects():
+    with pytest.raises(qkr.QkrError):
+        qkr.group_norm_silu_schedule(1, 30, 64, 4)          # groups does not divide channels
+    with pytest.raises(qkr.QkrError):
+        qkr.group_norm_silu_schedule(1, 8, 12, 2)           # spatial not a multiple of 8
+    lib = qkr.load_library()
+    assert lib.dit_group_norm_silu_schedule(1, 8, 64, 2, None) == 0      # the size out-pointer is optional
+

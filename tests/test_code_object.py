@@ -61,7 +61,7 @@ def _kernels(tmp_path):
 
 def _family(name):
     for fam in ("qknorm_rope_kernel", "fuse_scale_shift_kernel", "gn_single_kernel",
-                "gn_stats_kernel", "gn_apply_kernel"):
+                "gn_stats_kernel", "gn_apply_kernel", "gn_lagged_kernel", "gn_clear_kernel"):
         if fam in name:
             return fam
     return name
@@ -85,6 +85,8 @@ def test_every_source_file_contributes_its_kernels(kernels):
     assert fams.get("gn_single_kernel") == 6, fams   # 2 data dtypes x 3 affine dtypes
     assert fams.get("gn_apply_kernel") == 18, fams   # ... x 3 chunk sizes
     assert fams.get("gn_stats_kernel") == 6, fams    # 2 data dtypes x 3 chunk sizes
+    assert fams.get("gn_lagged_kernel") == 6, fams   # 2 data dtypes x 3 affine dtypes
+    assert fams.get("gn_clear_kernel") == 1, fams
 
 
 def test_no_kernel_uses_scratch_or_spills(kernels):

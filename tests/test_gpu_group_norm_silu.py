@@ -313,30 +313,35 @@ def test_maximum_workgroups():
     print("maximum workgroups max_abs", m)
 
 
-# (n, channels, spatial, groups, vectors per thread or 0 for one chunk per group)
+# (n, channels, spatial, groups, vectors per thread or 0 for one chunk per group, schedule)
 GN_SWEEP = [
-    (2, 64, 512, 32, 0),            # 1,024-element groups: the single-read kernel
-    (4, 512, 16384, 32, 8),         # channels of exactly one 16,384-element chunk
-    (4, 512, 16392, 32, 8),         # channel boundaries inside chunks (two-channel select)
-    (64, 512, 1000, 8, 8),          # channels shorter than a chunk (per-vector division)
-    (2, 512, 16384, 32, 4),         # 2,048 workgroups only with 8,192-element chunks
-    (1, 512, 16384, 32, 2),         # ... only with 4,096-element chunks
+    (2, 64, 512, 32, 0, "one_read"),        # 1,024-element groups
+    (4, 512, 16384, 32, 8, "two_pass"),     # channels of exactly one 16,384-element chunk
+    (4, 512, 16392, 32, 8, "two_pass"),     # channel boundaries inside chunks (two-channel select)
+    (64, 512, 1000, 8, 8, "two_pass"),      # channels shorter than a chunk (per-vector division)
+    (2, 512, 16384, 32, 4, "two_pass"),     # 2,048 workgroups only with 8,192-element chunks
+    (1, 512, 16384, 32, 2, "two_pass"),     # ... only with 4,096-element chunks
+    (8, 512, 16384, 32, 8, "lagged"),       # 4,096 chunks: the lagged single read
+    (8, 512, 16392, 32, 8, "lagged"),       # ... channel boundaries inside chunks
+    (128, 512, 1000, 8, 8, "lagged"),       # ... channels shorter than a chunk
 ]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("param", ["fp32", "bf16", "fp16"])
 def test_every_kernel_instantiation(dtype, param):
-    """Every compiled kernel of one (data, affine) dtype pair: the single-read
-    kernel, and the stats + apply pair at each chunk size, with channels
-    longer and shorter than a chunk.  The chunk size is confirmed through the
+    """Every compiled kernel of one (data, affine) dtype pair: the one-read
+    kernel, the stats + apply pair at each chunk size and the lagged kernel,
+    with channels longer and shorter than a chunk.  The chunk size is confirmed through the
     workspace size it implies; sampled groups against the oracle.  Samples
     repeat a block of at most 2 (the step is per group)."""
-    for n, channels, spatial, groups, vpt in GN_SWEEP:
+    for n, channels, spatial, groups, vpt, sched in GN_SWEEP:
         gsize = channels // groups * spatial
         chunk = 2048 * vpt
         want_ws = 0 if vpt == 0 else n * groups * -(-gsize // chunk) * 8
         assert qkr.group_norm_silu_workspace_size(n, channels, spatial, groups) == want_ws
+        assert qkr.group_norm_silu_schedule(n, channels, spatial, groups) == (sched,
+                                                                             chunk or 16384)
         nb = min(n, 2)
         block, g, b = wl.gn_inputs(7000 + spatial + n, nb, channels, spatial, dtype, param)
         blk = block.to(DEV)
@@ -353,3 +358,128 @@ def test_every_kernel_instantiation(dtype, param):
         # per-group bounds; the RNE-agreement fraction over all sampled groups
         check_groups(np.concatenate(got), np.concatenate(ref), gsize, dtype,
                      "%s vpt %d" % ((n, channels, spatial, groups), vpt))
+
+
+# ---------------------------------------------------------------- lagged schedule
+
+LAGGED = (8, 512, 16384, 32)            # 256 groups of 16 chunks: 4,096 chunks
+
+
+def _lagged_inputs(seed, dtype="bf16", param="fp32", shape=LAGGED):
+    n, channels, spatial, groups = shape
+    assert qkr.group_norm_silu_schedule(n, channels, spatial, groups)[0] == "lagged"
+    x, g, b = wl.gn_inputs(seed, n, channels, spatial, dtype, param)
+    return x, g, b
+
+
+@pytest.mark.parametrize("spatial", [16384, 16392])
+def test_lagged_and_two_pass_give_identical_bits(spatial):
+    """The first 4 samples of an 8-sample call (lagged) equal a 4-sample call
+    of the same samples (two passes) bit for bit: both combine the same chunk
+    partials in the same order."""
+    n, channels, groups = 8, 512, 32
+    assert qkr.group_norm_silu_schedule(n, channels, spatial, groups)[0] == "lagged"
+    assert qkr.group_norm_silu_schedule(4, channels, spatial, groups) == ("two_pass", 16384)
+    x, g, b = wl.gn_inputs(8100 + spatial, n, channels, spatial, "bf16", "fp32")
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    lagged = qkr.group_norm_silu(xd, gd, bd, groups)
+    two = qkr.group_norm_silu(xd[:4].contiguous(), gd, bd, groups)
+    torch.cuda.synchronize()
+    assert torch.equal(lagged[:4].view(torch.int16), two.view(torch.int16))
+
+
+def test_lagged_in_place_and_any_workspace_contents():
+    """In place equals out of place bit for bit, whatever the workspace held
+    before the call (all ones is the unpublished mark itself, zeros would
+    read as published statistics); sampled groups against the oracle."""
+    n, channels, spatial, groups = LAGGED
+    x, g, b = _lagged_inputs(8200)
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    need = qkr.group_norm_silu_workspace_size(n, channels, spatial, groups)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    outs = []
+    for fill in (0x00, 0x7F, 0xFF):
+        ws.fill_(fill)
+        outs.append(qkr.group_norm_silu(xd, gd, bd, groups, workspace=ws))
+    xi = xd.clone()
+    ws.fill_(0x00)
+    qkr.group_norm_silu(xi, gd, bd, groups, out=xi, workspace=ws)
+    torch.cuda.synchronize()
+    for o in outs[1:] + [xi]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    gsize = channels // groups * spatial
+    flat = outs[0].view(-1)
+    for q in (0, 1, 127, n * groups - 1):
+        ref = oracle_groups(x, "bf16", channels, spatial, groups, g, b, wl.EPS, q, q + 1)
+        check_groups(_decode(flat[q * gsize:(q + 1) * gsize], "bf16"), ref, gsize, "bf16",
+                     "lagged group %d" % q)
+
+
+@pytest.mark.parametrize("shape", [LAGGED, (1, 128, 1024 * 1024, 32)])
+def test_lagged_waiters_that_reduce_chunks_themselves(monkeypatch, shape):
+    """With no polling allowed (QKR_GN_WAIT_POLLS=0) every workgroup whose
+    group is not complete at its first look reduces the missing chunks
+    itself, racing their own workgroups; the first word published stands.
+    Out of place and in place, the bits equal the default call's."""
+    n, channels, spatial, groups = shape
+    x, g, b = _lagged_inputs(8300, shape=shape)
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    want = qkr.group_norm_silu(xd, gd, bd, groups)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("QKR_GN_WAIT_POLLS", "0")
+    for _ in range(3):
+        got = qkr.group_norm_silu(xd, gd, bd, groups)
+        xi = xd.clone()
+        torch.cuda.synchronize()
+        qkr.group_norm_silu(xi, gd, bd, groups, out=xi)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+        assert torch.equal(xi.view(torch.int16), want.view(torch.int16))
+
+
+def test_lagged_graph_capture_replays_match_eager():
+    """The clear kernel and the lagged kernel recorded into a graph: every
+    replay, with the workspace overwritten and eager work between replays,
+    equals the eager result."""
+    n, channels, spatial, groups = LAGGED
+    x, g, b = _lagged_inputs(8400)
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    eager = qkr.group_norm_silu(xd, gd, bd, groups)
+    ws = torch.empty(qkr.group_norm_silu_workspace_size(n, channels, spatial, groups),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(xd)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            qkr.group_norm_silu(xd, gd, bd, groups, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for fill in (0x00, 0x7F, 0xFF):
+        out.zero_()
+        ws.fill_(fill)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+def test_lagged_calls_on_concurrent_streams():
+    """Four lagged calls on four streams at once (own workspaces): each equals
+    the same call run alone."""
+    n, channels, spatial, groups = LAGGED
+    cases = []
+    for i in range(4):
+        x, g, b = _lagged_inputs(8500 + i)
+        xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+        alone = qkr.group_norm_silu(xd, gd, bd, groups)
+        torch.cuda.synchronize()
+        cases.append((xd, gd, bd, alone, torch.cuda.Stream()))
+    outs = []
+    for xd, gd, bd, _, st in cases:
+        with torch.cuda.stream(st):
+            outs.append(qkr.group_norm_silu(xd, gd, bd, groups, stream=st))
+    torch.cuda.synchronize()
+    for (_, _, _, alone, _), out in zip(cases, outs):
+        assert torch.equal(out.view(torch.int16), alone.view(torch.int16))
+

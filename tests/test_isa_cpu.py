@@ -54,7 +54,7 @@ def test_every_kernel_disassembled(disassembly):
     names = list(disassembly)
     assert sum("qknorm_rope_kernel" in n for n in names) == 336
     assert sum("fuse_scale_shift_kernel" in n for n in names) == 192
-    assert sum("gn_" in n for n in names) == 30
+    assert sum("gn_" in n for n in names) == 37
 
 
 def test_no_scalar_cache_writes(disassembly):
