@@ -8,10 +8,11 @@ one shared fp32 cos/sin row per token.
 Prints ONE JSON line.  ``dtype`` is the arithmetic type of the kernels (fp32:
 16-bit data are widened exactly, computed in fp32 and rounded once);
 ``config.data_dtype`` is the storage type.  ``value`` is achieved algorithmic
-HBM throughput over the K timed steps (GB/s, bytes the pass must move / time);
-``roofline.achieved`` uses the mean kernel duration from HIP events recorded
-around each launch on the launch stream; ``cpu_baseline`` times the fp64 CPU
-oracle on a bounded sample of the same workload.
+HBM throughput over the K timed steps, launched back to back (GB/s, bytes the
+pass must move / time); ``roofline.achieved`` uses the mean kernel duration
+from HIP events recorded around each launch on the launch stream, in a second
+pass of K launches; ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of the same workload.
 
   python bench.py --op fuse_scale_shift [--workload adaln_wan|adaln_flux|adaln_wan_cfg2]
                   [--dtype bf16|fp16] [--mod-dtype fp32|bf16|fp16] [--inplace] [--flush]
@@ -306,7 +307,15 @@ def cpu_baseline_gn(x_cpu, w, g, b, param_dtype, dtype, nbytes, budget_s):
 
 
 def time_launches(launch, stream, steps, warmup, flush_buf=None):
-    """Warm up, then time `steps` launches with HIP events on `stream`.
+    """Warm up, then time `steps` launches on `stream`.
+
+    Without flushing, two passes of `steps` launches each:
+    1. back to back, bracketed only by a barrier, a synchronisation and one
+       HIP event pair on `stream` (whole-job time: region ms and wall s);
+    2. with a HIP event pair around every launch (per-launch µs).
+    The per-launch events add a little host and queue work per launch, so
+    they stay out of the whole-job region.  With `flush_buf`, one pass: the
+    buffer is rewritten before every launch, outside its event pair.
 
     Returns (per-launch µs array, region ms, wall s)."""
     import numpy as np
@@ -315,12 +324,22 @@ def time_launches(launch, stream, steps, warmup, flush_buf=None):
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
+    if flush_buf is None:
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        region0.record(stream)
+        for _ in range(steps):
+            launch()
+        region1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        region_ms = region0.elapsed_time(region1)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
+    wall1 = time.perf_counter()
     region0.record(stream)
     for i in range(steps):
         if flush_buf is not None:
@@ -331,9 +350,11 @@ def time_launches(launch, stream, steps, warmup, flush_buf=None):
         ends[i].record(stream)
     region1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    if flush_buf is not None:
+        wall = time.perf_counter() - wall1
+        region_ms = region0.elapsed_time(region1)
     per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3
-    return per, region0.elapsed_time(region1), wall
+    return per, region_ms, wall
 
 
 def bench_fuse_scale_shift(args):
@@ -629,32 +650,8 @@ def main():
         qkr.qknorm_rope_fused(**tensors, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS,
                               style=style, cos_layout=args.layout, stream=handle)
 
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        launch()
-    torch.cuda.synchronize()
-
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    region0 = torch.cuda.Event(enable_timing=True)
-    region1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    region0.record(stream)
-    for i in range(K):
-        if flush_buf is not None:
-            with torch.cuda.stream(stream):
-                flush_buf.fill_(float(i))
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    region1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    region_ms = region0.elapsed_time(region1)
-    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3   # µs
+    per, region_ms, wall = time_launches(launch, stream, K, args.warmup, flush_buf)
     graph_us = graph_call_us(launch, stream, K) if args.graph and not args.flush else None
     mean_us = float(per.mean())
     achieved = nbytes / (mean_us * 1e-6) / 1e9
