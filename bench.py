@@ -432,6 +432,7 @@ def bench_group_norm_silu(args):
     gd, bd = g.to(dev), b.to(dev)
     y = x if args.inplace else torch.empty_like(x)
     need = qkr.group_norm_silu_workspace_size(w.n, w.channels, w.spatial, w.groups)
+    sched, chunk = qkr.group_norm_silu_schedule(w.n, w.channels, w.spatial, w.groups)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     pbytes = 4 if args.mod_dtype == "fp32" else 2
     nbytes = wl.gn_bytes(w.n, w.channels, w.spatial, param_bytes=pbytes)
@@ -458,7 +459,8 @@ def bench_group_norm_silu(args):
                                   args.mod_dtype, ", in place" if args.inplace else "",
                                   ", cache flushed" if args.flush else ""),
                    "n": w.n, "channels": w.channels, "spatial": w.spatial, "groups": w.groups,
-                   "workspace_bytes": need, "data_dtype": dtype, "parallelism": "single GPU"},
+                   "schedule": sched, "chunk_elems": chunk, "workspace_bytes": need,
+                   "data_dtype": dtype, "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
                         "p10": round(float(np.percentile(per, 10)), 2),
                         "p90": round(float(np.percentile(per, 90)), 2)},
