@@ -291,6 +291,11 @@ def test_group_norm_zero_samples_is_a_no_op():
     (4, 512, 16384, 32, ("two_pass", 16384)),          # 2,048 chunks: below the lagged threshold
     (1, 512, 128 * 128, 32, ("two_pass", 4096)),       # VAE mid: small chunks fill the chip
     (1, 64, 2048 * 2048, 32, ("two_pass", 16384)),     # 512 chunks per group: over 256
+    (1, 32, 256 * 16384, 32, ("lagged", 16384)),       # exactly 256 chunks per group
+    (1, 32, 257 * 16384, 32, ("two_pass", 16384)),     # 257 chunks per group
+    (4096, 8, 2 * 16384, 4, ("lagged", 16384)),        # 16,384 groups of 4 chunks
+    (1, 1365, 3 * 16384, 1365, ("two_pass", 16384)),   # 1,365 groups of 3 chunks: 4,095
+    (1, 2048, 16392, 2048, ("lagged", 16384)),         # 2,048 groups of 2 chunks: 4,096
 ])
 def test_group_norm_schedule_by_shape(n, channels, spatial, groups, want):
     assert qkr.group_norm_silu_schedule(n, channels, spatial, groups) == want

@@ -415,14 +415,18 @@ def test_lagged_in_place_and_any_workspace_contents():
                      "lagged group %d" % q)
 
 
-@pytest.mark.parametrize("shape", [LAGGED, (1, 128, 1024 * 1024, 32)])
-def test_lagged_waiters_that_reduce_chunks_themselves(monkeypatch, shape):
+@pytest.mark.parametrize("shape,dtype,param", [
+    (LAGGED, "bf16", "fp32"),
+    ((1, 128, 1024 * 1024, 32), "bf16", "fp32"),     # VAE out: 256 chunks per group
+    ((8, 512, 16392, 32), "fp16", "bf16"),           # channel boundaries inside chunks
+])
+def test_lagged_waiters_that_reduce_chunks_themselves(monkeypatch, shape, dtype, param):
     """With no polling allowed (QKR_GN_WAIT_POLLS=0) every workgroup whose
     group is not complete at its first look reduces the missing chunks
     itself, racing their own workgroups; the first word published stands.
     Out of place and in place, the bits equal the default call's."""
     n, channels, spatial, groups = shape
-    x, g, b = _lagged_inputs(8300, shape=shape)
+    x, g, b = _lagged_inputs(8300, dtype, param, shape=shape)
     xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
     want = qkr.group_norm_silu(xd, gd, bd, groups)
     torch.cuda.synchronize()
