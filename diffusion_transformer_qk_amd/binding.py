@@ -207,6 +207,10 @@ def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
         tokens = ref.numel() // (heads * head_dim) if ref.numel() else 0
         if q is not None and k is not None and (q.shape != k.shape or q.dtype != k.dtype):
             raise ValueError("q and k must have the same shape and dtype")
+    if cos_layout not in LAYOUTS:
+        raise ValueError("cos_layout must be one of %s" % sorted(LAYOUTS))
+    if style not in STYLES:
+        raise ValueError("style must be one of %s" % sorted(STYLES))
     if cos is None or sin is None:
         raise ValueError("cos and sin are required")
     if cos.dtype != sin.dtype or cos.shape != sin.shape:

@@ -162,6 +162,10 @@ def test_python_binding_rejects_cpu_tensors():
         qkr.qknorm_rope_fused(q=q, q_gamma=g, cos=c, sin=c, heads=4)
     with pytest.raises(ValueError, match="heads, head_dim"):
         qkr.qknorm_rope_fused(q=q.view(4, 128), q_gamma=g, cos=c, sin=c, heads=2, head_dim=64)
+    with pytest.raises(ValueError, match="style"):             # an unknown name, not a KeyError
+        qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c, style="neox")
+    with pytest.raises(ValueError, match="cos_layout"):
+        qkr.qknorm_rope_fused(x, q_gamma=g, k_gamma=g, cos=c, sin=c, cos_layout="expanded")
 
 
 # ----------------------------------------------------------------------------- AdaLN entry point
