@@ -1,0 +1,53 @@
+"""bench.py's one-line JSON report, end to end on the GPU (a few steps).
+
+The report's fields are a contract with the tools that read it: the metric,
+the whole-job value and its unit, the run's shape, the roofline object of the
+dominant kernel and the CPU-oracle baseline.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                         capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = [l for l in out.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, out.stdout
+    return json.loads(lines[0])
+
+
+def test_default_report_carries_every_field():
+    r = run_bench("--steps", "5", "--warmup", "2", "--cpu-seconds", "0.2")
+    assert r["metric"].startswith("QK-norm+RoPE")
+    assert r["unit"] == "GB/s" and r["value"] > 0
+    assert (r["n_gpus"], r["steps"], r["warmup"]) == (1, 5, 2)
+    assert r["higher_is_better"] is True and r["scaling"] == "weak"
+    assert r["vs_baseline"] is None and r["data"] == "synthetic" and r["dtype"] == "f32"
+    assert r["ms_per_step"] > 0
+    cfg = r["config"]
+    assert cfg["workload"].startswith("headline") and (cfg["tokens"], cfg["heads"],
+                                                        cfg["head_dim"]) == (32760, 40, 128)
+    roof = r["roofline"]
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert roof["traffic"] is None or roof["traffic"] > 0
+    cpu = r["cpu_baseline"]
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["value"] > 0
+    assert cpu["cores"] >= 1 and cpu["sample"]
+    assert r["kernel"]["scratch_bytes"] == 0
+
+
+@pytest.mark.parametrize("op", ["fuse_scale_shift", "group_norm_silu"])
+def test_step_reports(op):
+    r = run_bench("--op", op, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    assert r["unit"] == "GB/s" and r["value"] > 0 and r["roofline"]["bound"] == "hbm"
+    assert r["config"]["parallelism"] == "single GPU"
