@@ -153,17 +153,20 @@ def _call_context(ref, tensors, stream):
     current device, so a NULL (default) stream means that device's.
     """
     torch = _torch()
+    dev = ref.device
     for t in tensors:
-        if t is not None and t.device != ref.device:
-            raise ValueError("all tensors must be on one device (%s)" % ref.device)
+        if t is not None and t.device != dev:
+            raise ValueError("all tensors must be on one device (%s)" % dev)
     if stream is None:
-        raw = torch.cuda.current_stream(ref.device).cuda_stream if ref.is_cuda else 0
+        raw = torch.cuda.current_stream(dev).cuda_stream if ref.is_cuda else 0
     elif isinstance(stream, int):
         raw = stream
     else:
         raw = stream.cuda_stream
-    ctx = torch.cuda.device(ref.device) if ref.is_cuda else contextlib.nullcontext()
-    return ctx, raw
+    # switching the current device costs a few µs per call: only when needed
+    if ref.is_cuda and dev.index != torch.cuda.current_device():
+        return torch.cuda.device(dev), raw
+    return contextlib.nullcontext(), raw
 
 
 def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
