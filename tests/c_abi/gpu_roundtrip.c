@@ -7,7 +7,10 @@
  * qknorm_rope_fused runs in place with one shared fp32 cos/sin row per token
  * (interleaved pairs); the result comes back and every Q and K element is
  * compared with the fp64 oracle (max_abs <= 1.6e-2, bf16), and every V element
- * bit for bit with the input.  Prints "ok max_abs <value>" and exits 0. */
+ * bit for bit with the input.  Then the AdaLN modulation (two batches) and
+ * group norm + SiLU in its two-pass and lagged schedules, with the workspace
+ * sized by its query, each against the oracle (within (max |ref| + 1) / 256).
+ * Prints each step's max_abs, then "ok", and exits 0. */
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -16,13 +19,22 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "fuse_scale_shift.h"
+#include "group_norm_silu.h"
 #include "qknorm_rope.h"
 
-/* the oracle's entry point (libqkr_oracle.so; dtype codes bf16 0, fp32 2) */
+/* the oracle's entry points (libqkr_oracle.so; dtype codes bf16 0, fp32 2) */
 int qkr_oracle_qknorm_rope(const uint16_t* x, int x_dtype, int64_t row_stride, int64_t col0,
                            int64_t t_begin, int64_t t_end, int32_t heads, int32_t head_dim,
                            const float* gamma, float eps, const void* cos, const void* sin,
                            int cos_dtype, int cos_layout, int style, double* out);
+int qkr_oracle_adaln(const uint16_t* x, int x_dtype, int64_t row_begin, int64_t row_end,
+                     int64_t hidden, int64_t rows_per_batch, const void* scale, const void* shift,
+                     int mod_dtype, float eps, double* out);
+int qkr_oracle_group_norm_silu(const uint16_t* x, int x_dtype, int64_t channels, int64_t spatial,
+                               int64_t groups, int64_t group_begin, int64_t group_end,
+                               const void* gamma, const void* beta, int param_dtype, float eps,
+                               double* out);
 
 static uint32_t next_u32(uint32_t* s)
 {
@@ -60,7 +72,151 @@ static double double_of_bf16(uint16_t b)
         }                                                                       \
     } while (0)
 
+/* max |got - ref| over n outputs, or -1 if one exceeds (max |ref| + 1) / 256
+ * (half a bf16 ulp at the largest output, with margin, as in the smoke check) */
+static double check_bf16(const uint16_t* got, const double* ref, int64_t n)
+{
+    double big = 0.0, worst = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        if (fabs(ref[i]) > big)
+            big = fabs(ref[i]);
+    for (int64_t i = 0; i < n; ++i) {
+        const double err = fabs(double_of_bf16(got[i]) - ref[i]);
+        if (!(err <= (big + 1.0) / 256.0))
+            return -1.0;
+        if (err > worst)
+            worst = err;
+    }
+    return worst;
+}
+
+/* AdaLN modulation: 37 rows of 1000 in 2 batches (19 rows each), fp32 scale/shift */
+static int adaln(uint32_t* seed)
+{
+    enum { R = 37, C = 1000, RPB = 19, B = 2 };
+    uint16_t* x = malloc((size_t)R * C * 2);
+    uint16_t* y = malloc((size_t)R * C * 2);
+    float* sc = malloc((size_t)B * C * 4);
+    float* sh = malloc((size_t)B * C * 4);
+    double* ref = malloc((size_t)R * C * sizeof(double));
+    if (!x || !y || !sc || !sh || !ref)
+        return printf("FAIL host allocation\n"), 1;
+    for (int i = 0; i < R * C; ++i)
+        x[i] = bf16_of((uniform(seed) * 2.0f - 1.0f) * 2.0f + 0.5f);
+    for (int i = 0; i < B * C; ++i) {
+        sc[i] = (uniform(seed) * 2.0f - 1.0f) * 0.5f;
+        sh[i] = (uniform(seed) * 2.0f - 1.0f) * 0.5f;
+    }
+    void *dx, *dy, *dsc, *dsh;
+    CHECK_HIP(hipMalloc(&dx, (size_t)R * C * 2));
+    CHECK_HIP(hipMalloc(&dy, (size_t)R * C * 2));
+    CHECK_HIP(hipMalloc(&dsc, (size_t)B * C * 4));
+    CHECK_HIP(hipMalloc(&dsh, (size_t)B * C * 4));
+    CHECK_HIP(hipMemcpy(dx, x, (size_t)R * C * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dsc, sc, (size_t)B * C * 4, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dsh, sh, (size_t)B * C * 4, hipMemcpyHostToDevice));
+    const int rc = dit_fuse_scale_shift(dx, dy, R, C, RPB, dsc, dsh, QKR_FP32, 1e-6f, QKR_BF16, NULL);
+    if (rc != QKR_OK)
+        return printf("FAIL dit_fuse_scale_shift: %s\n", qknorm_rope_strerror(rc)), 1;
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(y, dy, (size_t)R * C * 2, hipMemcpyDeviceToHost));
+    if (qkr_oracle_adaln(x, 0, 0, R, C, RPB, sc, sh, 2, 1e-6f, ref) != 0)
+        return printf("FAIL adaln oracle\n"), 1;
+    const double worst = check_bf16(y, ref, (int64_t)R * C);
+    if (worst < 0)
+        return printf("FAIL adaln output outside the bound\n"), 1;
+    printf("adaln max_abs %.4g\n", worst);
+    CHECK_HIP(hipFree(dx));
+    CHECK_HIP(hipFree(dy));
+    CHECK_HIP(hipFree(dsc));
+    CHECK_HIP(hipFree(dsh));
+    free(x), free(y), free(sc), free(sh), free(ref);
+    return 0;
+}
+
+/* group norm + SiLU on [n, channels, spatial] with `groups` groups, fp32
+ * affine, workspace from the size query; the oracle checks the first and
+ * last group */
+static int group_norm(uint32_t* seed, int64_t n, int32_t channels, int64_t spatial,
+                      int32_t groups, int32_t want_schedule)
+{
+    const int64_t count = n * channels * spatial, gsize = channels / groups * spatial;
+    const int64_t pairs = n * groups;
+    uint16_t* x = malloc((size_t)count * 2);
+    uint16_t* y = malloc((size_t)count * 2);
+    float* g = malloc((size_t)channels * 4);
+    float* b = malloc((size_t)channels * 4);
+    double* ref = malloc((size_t)gsize * sizeof(double));
+    if (!x || !y || !g || !b || !ref)
+        return printf("FAIL host allocation\n"), 1;
+    for (int64_t i = 0; i < count; ++i)
+        x[i] = bf16_of((uniform(seed) * 2.0f - 1.0f) * 3.0f + 1.0f);
+    for (int c = 0; c < channels; ++c) {
+        g[c] = 1.0f + 0.2f * (uniform(seed) * 2.0f - 1.0f);
+        b[c] = 0.3f * (uniform(seed) * 2.0f - 1.0f);
+    }
+    int64_t chunk = 0;
+    const int32_t schedule = dit_group_norm_silu_schedule(n, channels, spatial, groups, &chunk);
+    if (schedule != want_schedule)
+        return printf("FAIL schedule %d, want %d\n", schedule, want_schedule), 1;
+    const int64_t ws_bytes = dit_group_norm_silu_workspace_size(n, channels, spatial, groups);
+    if (ws_bytes < 0)
+        return printf("FAIL workspace size %lld\n", (long long)ws_bytes), 1;
+    void *dx, *dy, *dg, *db, *ws = NULL;
+    CHECK_HIP(hipMalloc(&dx, (size_t)count * 2));
+    CHECK_HIP(hipMalloc(&dy, (size_t)count * 2));
+    CHECK_HIP(hipMalloc(&dg, (size_t)channels * 4));
+    CHECK_HIP(hipMalloc(&db, (size_t)channels * 4));
+    if (ws_bytes > 0)
+        CHECK_HIP(hipMalloc(&ws, (size_t)ws_bytes));
+    CHECK_HIP(hipMemcpy(dx, x, (size_t)count * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(dg, g, (size_t)channels * 4, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(db, b, (size_t)channels * 4, hipMemcpyHostToDevice));
+    const int rc = dit_group_norm_silu(dx, dy, n, channels, spatial, groups, dg, db, QKR_FP32,
+                                       1e-6f, QKR_BF16, ws, ws_bytes, NULL);
+    if (rc != QKR_OK)
+        return printf("FAIL dit_group_norm_silu: %s\n", qknorm_rope_strerror(rc)), 1;
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(y, dy, (size_t)count * 2, hipMemcpyDeviceToHost));
+    double worst = 0.0;
+    const int64_t check[2] = {0, pairs - 1};
+    for (int i = 0; i < 2; ++i) {
+        const int64_t q = check[i];
+        if (qkr_oracle_group_norm_silu(x, 0, channels, spatial, groups, q, q + 1, g, b, 2, 1e-6f,
+                                       ref) != 0)
+            return printf("FAIL group-norm oracle\n"), 1;
+        const double w = check_bf16(y + q * gsize, ref, gsize);
+        if (w < 0)
+            return printf("FAIL group %lld outside the bound\n", (long long)q), 1;
+        if (w > worst)
+            worst = w;
+    }
+    printf("group_norm_silu schedule %d chunk %lld max_abs %.4g\n", schedule, (long long)chunk,
+           worst);
+    CHECK_HIP(hipFree(dx));
+    CHECK_HIP(hipFree(dy));
+    CHECK_HIP(hipFree(dg));
+    CHECK_HIP(hipFree(db));
+    if (ws)
+        CHECK_HIP(hipFree(ws));
+    free(x), free(y), free(g), free(b), free(ref);
+    return 0;
+}
+
+static int qk_pass(uint32_t* seed_in);
+
 int main(void)
+{
+    uint32_t seed = 20251202u;
+    if (qk_pass(&seed) || adaln(&seed) || group_norm(&seed, 2, 8, 8192, 2, 2) ||
+        group_norm(&seed, 8, 512, 16384, 32, 1))
+        return 1;
+    printf("ok\n");
+    return 0;
+}
+
+/* the fused pass on a fused QKV buffer; returns 0 and prints max_abs */
+static int qk_pass(uint32_t* seed_in)
 {
     enum { T = 37, H = 3, D = 128 };
     const int64_t width = 3 * H * D;
@@ -76,7 +232,7 @@ int main(void)
         printf("FAIL host allocation\n");
         return 1;
     }
-    uint32_t seed = 20251202u;
+    uint32_t seed = *seed_in;
     for (int64_t i = 0; i < T * width; ++i)
         x[i] = bf16_of((uniform(&seed) * 2.0f - 1.0f) * 3.0f);
     for (int d = 0; d < D; ++d) {
@@ -142,6 +298,8 @@ int main(void)
     CHECK_HIP(hipFree(dkg));
     CHECK_HIP(hipFree(dc));
     CHECK_HIP(hipFree(ds));
-    printf("ok max_abs %.4g\n", max_abs);
+    free(x), free(back), free(qg), free(kg), free(cs), free(sn), free(ref);
+    *seed_in = seed;
+    printf("qknorm_rope max_abs %.4g\n", max_abs);
     return 0;
 }

@@ -3,7 +3,9 @@
 gcc builds tests/c_abi/gpu_roundtrip.c against include/qknorm_rope.h, HIP's C
 runtime API, the built libqknorm_rope.so and the CPU oracle; the program
 uploads a fused QKV buffer, calls qknorm_rope_fused, and checks Q and K
-against the oracle (bf16 bar, max_abs <= 1.6e-2) and V bit for bit.
+against the oracle (bf16 bar, max_abs <= 1.6e-2) and V bit for bit; then the
+AdaLN step and group norm + SiLU in its two-pass and lagged schedules, each
+against the oracle.
 """
 import os
 import shutil
@@ -32,5 +34,5 @@ def test_c_program_runs_the_pass_on_the_gpu(tmp_path, oracle_lib):
                     "-Wl,-rpath," + lib_dir, "-Wl,-rpath," + oracle_dir,
                     "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", exe], check=True)
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
-    assert out.returncode == 0 and out.stdout.startswith("ok"), out.stdout + out.stderr
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stdout + out.stderr
     print(out.stdout.strip())
