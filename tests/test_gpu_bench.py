@@ -51,3 +51,16 @@ def test_step_reports(op):
     r = run_bench("--op", op, "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
     assert r["unit"] == "GB/s" and r["value"] > 0 and r["roofline"]["bound"] == "hbm"
     assert r["config"]["parallelism"] == "single GPU"
+
+
+def test_graph_and_flush_modes():
+    """--graph adds the per-call time replayed from a captured HIP graph;
+    --flush rewrites 1 GiB before each call and reports the per-call rate."""
+    g = run_bench("--workload", "tiny", "--graph", "--steps", "20", "--warmup", "2",
+                  "--no-cpu-baseline")
+    assert g["graph_us_per_call"] > 0
+    f = run_bench("--workload", "mid", "--flush", "--steps", "5", "--warmup", "1",
+                  "--no-cpu-baseline")
+    assert "cache flushed" in f["config"]["workload"]
+    assert abs(f["value"] - f["roofline"]["achieved"]) <= 0.1
+
