@@ -227,10 +227,12 @@ def test_graph_capture_replays_match_eager():
 
 def test_byte_offsets_beyond_4gib_in_place():
     """[260, 128, 256, 256] bf16 = 4.4 GB in place, 32 groups of 16 chunks:
-    8320 groups (133,120 workgroups per pass); groups on both sides of the 2^32-byte offset
+    8320 groups, 133,120 chunks (the lagged schedule: 133,120 + 768
+    workgroups); groups on both sides of the 2^32-byte offset
     (group 8192 starts there) against the oracle.  The samples repeat a
     4-sample block."""
     n, channels, spatial, groups, B = 260, 128, 256 * 256, 32, 4
+    assert qkr.group_norm_silu_schedule(n, channels, spatial, groups)[0] == "lagged"
     block, g, b = wl.gn_inputs(4444, B, channels, spatial, "bf16", "fp32")
     blk = block.to(DEV)
     x = torch.empty((n, channels, spatial), dtype=torch.bfloat16, device=DEV)
