@@ -169,6 +169,22 @@ def _call_context(ref, tensors, stream):
     return contextlib.nullcontext(), raw
 
 
+def _launch_stream_context(ref, stream):
+    """Context in which tensors the binding allocates for a call belong to the
+    stream the call is launched on, so that the caching allocator hands their
+    memory to other work only in that stream's order (memory allocated on the
+    current stream and freed on return could be reused by the current stream
+    while the launch stream still uses it)."""
+    torch = _torch()
+    if stream is None or not ref.is_cuda:
+        return contextlib.nullcontext()
+    if isinstance(stream, int):
+        if stream == torch.cuda.current_stream(ref.device).cuda_stream:
+            return contextlib.nullcontext()
+        stream = torch.cuda.ExternalStream(stream, device=ref.device)
+    return torch.cuda.stream(stream)
+
+
 def qknorm_rope_fused(qkv=None, q=None, k=None, *, q_gamma=None, k_gamma=None,
                       cos=None, sin=None, eps: float = 1e-6, heads: int | None = None,
                       head_dim: int | None = None, cos_layout: str = "shared",
@@ -292,7 +308,8 @@ def fuse_scale_shift(x, scale, shift, *, out=None, eps: float = 1e-6,
     if rows and (rows - 1) // rows_per_batch >= batches:
         raise ValueError("scale/shift hold fewer batches than the rows need")
     if out is None:
-        out = torch.empty_like(x)
+        with _launch_stream_context(x, stream):
+            out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("out must match x in shape and dtype")
     ctx, stream_ptr = _call_context(x, (out, scale, shift), stream)
@@ -341,8 +358,9 @@ def group_norm_silu(x, gamma, beta, groups: int, *, out=None, eps: float = 1e-6,
     their product a multiple of 8).  ``gamma``/``beta``: [channels].
     ``workspace``: a device tensor of at least the queried size; when None and
     one is needed, a byte tensor is allocated here with torch (the library
-    itself never allocates).  ``out`` defaults to a new tensor; ``out=x``
-    works in place.
+    itself never allocates), on the launch stream, so its memory is not reused
+    before the call's kernels are done with it.  ``out`` defaults to a new
+    tensor (also on the launch stream); ``out=x`` works in place.
     """
     torch = _torch()
     if x.dim() < 3:
@@ -356,12 +374,13 @@ def group_norm_silu(x, gamma, beta, groups: int, *, out=None, eps: float = 1e-6,
     need = group_norm_silu_workspace_size(n, channels, spatial, groups) if x.numel() else 0
     if need < 0:
         raise QkrError(need, strerror(need))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with _launch_stream_context(x, stream):
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if out is None:
+            out = torch.empty_like(x)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if out is None:
-        out = torch.empty_like(x)
-    elif out.shape != x.shape or out.dtype != x.dtype:
+    if out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("out must match x in shape and dtype")
     ctx, stream_ptr = _call_context(x, (out, gamma, beta, workspace), stream)
     with ctx:

@@ -91,6 +91,14 @@ __device__ __forceinline__ void load_f32x8(const float* p, float f[8])
     }
 }
 
+// 1 / sqrt(x) for any positive x, subnormals included: the hardware
+// reciprocal square root takes a subnormal input as zero (and returns +inf),
+// so a subnormal x is scaled by 2^64 first (exact) and the result by 2^32.
+__device__ __forceinline__ float rsqrt_full_range(float x)
+{
+    return x < 0x1p-126f ? __builtin_amdgcn_rsqf(x * 0x1p64f) * 0x1p32f : __builtin_amdgcn_rsqf(x);
+}
+
 // Sum over all 64 lanes of a wave; every lane ends with the same value.
 __device__ __forceinline__ float wave_sum(float v)
 {
@@ -118,6 +126,34 @@ __device__ __forceinline__ float block_sum(float v, float* slot)
 #pragma unroll
     for (int w = 1; w < WAVES; ++w)
         t += slot[w];
+    return t;
+}
+
+// Largest value over all 64 lanes of a wave; every lane ends with it.
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Largest value over a workgroup of WAVES waves through `slot` (WAVES floats
+// of LDS); the same barrier and slot rules as block_sum.
+template <int WAVES>
+__device__ __forceinline__ float block_max(float v, float* slot)
+{
+    v = wave_max(v);
+    if (threadIdx.x % kWave == 0)
+        slot[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float t = slot[0];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w)
+        t = fmaxf(t, slot[w]);
     return t;
 }
 

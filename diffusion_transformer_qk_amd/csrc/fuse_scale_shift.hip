@@ -87,6 +87,21 @@ __device__ __forceinline__ float wave_total(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
+// Sums of squared deviations at or above this keep full fp32 precision;
+// below it subnormal squares lose bits, which only matters when eps is below
+// it too.
+constexpr float kTinySum = 0x1p-100f;
+
+// Whether the plain fp32 statistics of a row are usable: q = var + eps finite
+// (false when the sum or the squared deviations overflowed: 16-bit rows with
+// values beyond about 1e17, or NaN), and the sum of squared deviations ss
+// clear of the subnormal range or swamped by eps.  When true, q is at least
+// 2^-113, a normal number, as the hardware reciprocal square root needs.
+__device__ __forceinline__ bool stats_in_range(float ss, float q, float eps)
+{
+    return q <= 0x1.fffffep127f && (ss >= kTinySum || eps >= kTinySum);
+}
+
 // Make the compiler forget what v holds, so the fp32 values unpacked from it
 // are unpacked again for each pass instead of being kept alive across them.
 template <int VPT>
@@ -142,6 +157,91 @@ __device__ __forceinline__ void modulate_store(const FssParams& p, __amdgpu_buff
             for (int k = 0; k < 8; ++k)
                 o[k] = __builtin_fmaf((f[k] - mean) * rstd, 1.0f + s[k], h[k]);
             __builtin_amdgcn_raw_buffer_store_b128(pack8<X_FP16>(o), yr, i * 16, 0, kBufferNT);
+        }
+    }
+}
+
+// A row whose plain fp32 statistics are out of range (stats_in_range; the
+// branch is wave-uniform): with e the binary exponent of the row's largest
+// |x|, recompute mean and variance on x * 2^-e (an exact power-of-two
+// scaling, every term <= 1 in magnitude) and normalise x * 2^-e with them,
+// since (x - mean) / sqrt(var + eps) equals (x 2^-e - mean_e) / sqrt(var_e +
+// eps 2^-2e).  If eps 2^-2e overflows, the variance is below eps by more than
+// 2^128 and the plain mean with 1 / sqrt(eps) is exact to fp32.  Nothing of
+// the row is written yet, so this path reads it again from memory (a vector
+// at a time, the same vectors and order as the register passes) and leaves
+// the registers of the common path free.
+template <int VPT, bool X_FP16, int MOD>
+__device__ __forceinline__ void rescaled_row(const FssParams& p, int64_t r, const u32x4* staged,
+                                             bool from_lds, int64_t mrow, float mean)
+{
+    const int lane = threadIdx.x % kWave;
+    const int C = p.hidden;
+    const int nvec = C / kVec;
+    const int row_bytes = C * 2;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(p.x + r * C), 0, row_bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(p.y + r * C, 0, row_bytes, kBufferFlags);
+    // vectors past the row end read as zero (buffer range), like the loads
+    // of the register passes
+    float m = 0.0f;
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        float f[8];
+        unpack8<X_FP16>(__builtin_amdgcn_raw_buffer_load_b128(xr, (u * kWave + lane) * 16, 0, 0), f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            m = fmaxf(m, fabsf(f[k]));
+    }
+    const int e = __builtin_amdgcn_frexp_expf(wave_max(m));
+    const float eps_s = __builtin_amdgcn_ldexpf(p.eps, -2 * e);
+    float mean_s = mean, rstd = rsqrt_full_range(p.eps);
+    int shift = 0;
+    if (eps_s <= 0x1.fffffep127f) {
+        shift = e;
+        float sum = 0.0f;
+#pragma unroll 1
+        for (int u = 0; u < VPT; ++u) {
+            float f[8];
+            unpack8<X_FP16>(__builtin_amdgcn_raw_buffer_load_b128(xr, (u * kWave + lane) * 16, 0, 0), f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                sum += __builtin_amdgcn_ldexpf(f[k], -shift);
+        }
+        mean_s = wave_total(sum) / (float)C;
+        float ss = 0.0f;
+#pragma unroll 1
+        for (int u = 0; u < VPT; ++u) {
+            if (u * kWave + lane < nvec) {
+                float f[8];
+                unpack8<X_FP16>(__builtin_amdgcn_raw_buffer_load_b128(xr, (u * kWave + lane) * 16, 0, 0), f);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float d = __builtin_amdgcn_ldexpf(f[k], -shift) - mean_s;
+                    ss = __builtin_fmaf(d, d, ss);
+                }
+            }
+        }
+        // a constant row of large values has var_e = 0 and eps 2^-2e may
+        // underflow to 0: the floor keeps rstd finite for its zero deviations
+        rstd = __builtin_amdgcn_rsqf(fmaxf(wave_total(ss) / (float)C + eps_s, 0x1p-126f));
+    }
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kWave + lane;
+        if (i < nvec) {
+            float f[8], sc[8], sh[8], o[8];
+            unpack8<X_FP16>(__builtin_amdgcn_raw_buffer_load_b128(xr, i * 16, 0, 0), f);
+            if (from_lds)
+                mod_entries<MOD, true>(p, staged, nvec, 0, i, sc, sh);
+            else
+                mod_entries<MOD, false>(p, staged, nvec, mrow, i, sc, sh);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                o[k] = __builtin_fmaf((__builtin_amdgcn_ldexpf(f[k], -shift) - mean_s) * rstd,
+                                      1.0f + sc[k], sh[k]);
+            __builtin_amdgcn_raw_buffer_store_b128(pack8<X_FP16>(o), yr, i * 16, 0, 0);
         }
     }
 }
@@ -251,18 +351,25 @@ void fuse_scale_shift_kernel(const FssParams p)
             }
         }
     }
-    const float rstd = __builtin_amdgcn_rsqf(wave_total(ss) / (float)C + p.eps);
+    const float ss_row = wave_total(ss);
+    const float q = ss_row / (float)C + p.eps;
     forget_unpacked(v);
 
     // pass 3: normalise, modulate, round, store
     const __amdgpu_buffer_rsrc_t yr =
         __builtin_amdgcn_make_buffer_rsrc(p.y + r * C, 0, row_bytes, kBufferFlags);
     const uint32_t batch = (uint32_t)r / p.rows_per_batch;
-    if (WAVES > 1 && batch == staged_batch)
-        modulate_store<VPT, X_FP16, MOD, true, FULL>(p, yr, v, staged, nvec, 0, mean, rstd);
-    else
-        modulate_store<VPT, X_FP16, MOD, false, FULL>(p, yr, v, staged, nvec, (int64_t)batch * C,
-                                                      mean, rstd);
+    const bool from_lds = WAVES > 1 && batch == staged_batch;
+    const int64_t mrow = (int64_t)batch * C;
+    if (__builtin_expect(stats_in_range(ss_row, q, p.eps), 1)) {
+        const float rstd = __builtin_amdgcn_rsqf(q);
+        if (from_lds)
+            modulate_store<VPT, X_FP16, MOD, true, FULL>(p, yr, v, staged, nvec, 0, mean, rstd);
+        else
+            modulate_store<VPT, X_FP16, MOD, false, FULL>(p, yr, v, staged, nvec, mrow, mean, rstd);
+    } else {
+        rescaled_row<VPT, X_FP16, MOD>(p, r, staged, from_lds, mrow, mean);
+    }
 }
 
 using FssFn = void (*)(FssParams);

@@ -32,7 +32,6 @@
 
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "device_common.h"
 #include "host_common.h"
@@ -172,6 +171,105 @@ __device__ __forceinline__ void chunk_moments_streamed(const uint16_t* base, int
     m2 = block_sum<kWaves>(ss, red1);
 }
 
+// ------------------------------------------------------------ out-of-range statistics
+//
+// The plain fp32 statistics overflow for 16-bit groups whose values exceed
+// about 1e17 (squared deviations) or 1e34 (sums), and lose bits to subnormal
+// squares when the sums fall below kTinySum while eps is below it too.  Such
+// chunks and groups are recomputed on x * 2^-e, e the binary exponent of the
+// largest magnitude involved (an exact power-of-two scaling that brings every
+// term to at most 1), and normalised in that scale: (x - mean) / sqrt(var +
+// eps) equals (x 2^-e - mean_e) / sqrt(var_e + eps 2^-2e).  If eps 2^-2e
+// overflows, the variance is below eps by more than 2^128 and the plain mean
+// with 1 / sqrt(eps) is exact to fp32.
+constexpr float kTinySum = 0x1p-100f;
+constexpr float kFltMax = 0x1.fffffep127f;
+
+__device__ __forceinline__ bool moments_in_range(float m2, float eps)
+{
+    // false for an overflowed (inf) or NaN sum of squared deviations too
+    return m2 <= kFltMax && (m2 >= kTinySum || eps >= kTinySum);
+}
+
+// A group's normalisation: t = (x 2^-shift - mean) * rstd * gamma + beta.
+struct GroupStats {
+    float mean;
+    float rstd;
+    int shift;
+};
+
+// Statistics of a chunk (nv valid vectors at base) on x * 2^-e, read from
+// memory a vector at a time: e the exponent of the chunk's largest |x|,
+// mean_s and m2_s (sum of squared deviations) of the rescaled values.  Uses
+// three slots (red[0..2]); every thread gets the same bits.
+template <bool X_FP16, int VPT>
+__device__ __forceinline__ void chunk_moments_rescaled(const uint16_t* base, int nv, float (*red)[kWaves],
+                                                    int& e, float& mean_s, float& m2_s)
+{
+    float m = 0.0f;
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        if (i < nv) {
+            float f[8];
+            unpack8<X_FP16>(load16<false>(base + (int64_t)i * kVec), f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                m = fmaxf(m, fabsf(f[k]));
+        }
+    }
+    e = __builtin_amdgcn_frexp_expf(block_max<kWaves>(m, red[0]));
+    float sum = 0.0f;
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        if (i < nv) {
+            float f[8];
+            unpack8<X_FP16>(load16<false>(base + (int64_t)i * kVec), f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                sum += __builtin_amdgcn_ldexpf(f[k], -e);
+        }
+    }
+    mean_s = block_sum<kWaves>(sum, red[1]) / (float)(nv * kVec);
+    float ss = 0.0f;
+#pragma unroll 1
+    for (int u = 0; u < VPT; ++u) {
+        const int i = u * kBlock + threadIdx.x;
+        if (i < nv) {
+            float f[8];
+            unpack8<X_FP16>(load16<false>(base + (int64_t)i * kVec), f);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float d = __builtin_amdgcn_ldexpf(f[k], -e) - mean_s;
+                ss = __builtin_fmaf(d, d, ss);
+            }
+        }
+    }
+    m2_s = block_sum<kWaves>(ss, red[2]);
+}
+
+// A chunk's published partial: (mean, sum of squared deviations) as two fp32
+// words, or, for a chunk whose plain sum is out of range, (mean, -sd) with sd
+// the chunk's standard deviation (always a finite fp32 for finite data; the
+// sign bit of the second word marks this form).  `mean` and `m2` are the
+// plain statistics already computed; the chunk is read again only when they
+// are out of range.
+template <bool X_FP16, int VPT>
+__device__ __forceinline__ f32x2 chunk_partial(const GnParams& p, const uint16_t* base, int nv,
+                                               float mean, float m2, float (*red)[kWaves])
+{
+    if (__builtin_expect(moments_in_range(m2, p.eps), 1))
+        return f32x2{mean, m2};
+    int e;
+    float mean_s, m2_s;
+    chunk_moments_rescaled<X_FP16, VPT>(base, nv, red, e, mean_s, m2_s);
+    if (!(__builtin_amdgcn_ldexpf(p.eps, -2 * e) <= kFltMax))
+        return f32x2{mean, m2};     // the chunk's variance is nothing next to eps
+    const float sd = __builtin_amdgcn_ldexpf(__builtin_sqrtf(m2_s / (float)(nv * kVec)), e);
+    return f32x2{__builtin_amdgcn_ldexpf(mean_s, e), -sd};
+}
+
 template <int PARAM>
 __device__ __forceinline__ float param(const void* table, int c)
 {
@@ -187,18 +285,23 @@ __device__ __forceinline__ float param(const void* table, int c)
 }
 
 // Normalise, apply the channel affine and SiLU to the chunk, store it:
-// t = fma(x - mean, a[c], beta[c]) with a[c] = rstd * gamma[c] formed once
-// per channel, then y = t * rcp(1 + exp(-t)).  When a channel holds at least
-// a chunk, the chunk covers at most two channels: their coefficients come from
-// uniform addresses once, and each vector picks one by comparing its offset
-// with the channel boundary.  Otherwise each vector divides its offset by
-// spatial to find its channel.
-template <bool X_FP16, int PARAM, int VPT>
-__device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k, int nv,
-                                            const u32x4 (&v)[VPT], float mean, float rstd)
+// t = fma(x 2^-shift - mean, a[c], beta[c]) with a[c] = rstd * gamma[c]
+// formed once per channel, then y = t * rcp(1 + exp(-t)).  When a channel
+// holds at least a chunk, the chunk covers at most two channels: their
+// coefficients come from uniform addresses once, and each vector picks one by
+// comparing its offset with the channel boundary.  Otherwise each vector
+// divides its offset by spatial to find its channel.  The chunk comes from
+// the registers v (st.shift == 0) or, for statistics taken in a rescaled
+// form (RESCALED), from memory a vector at a time: it is not written yet, and
+// each thread reads a vector before it writes it.
+template <bool X_FP16, int PARAM, int VPT, bool RESCALED>
+__device__ __forceinline__ void chunk_apply_as(const GnParams& p, int64_t q, int k, int nv,
+                                               const u32x4 (&v)[VPT], const GroupStats& st)
 {
     constexpr int64_t kChunk = chunk_elems<VPT>();
+    const float mean = st.mean, rstd = st.rstd;
     uint16_t* yq = p.y + q * p.group_size + (int64_t)k * kChunk;
+    const uint16_t* xq = p.x + q * p.group_size + (int64_t)k * kChunk;
     const int c0 = (int)(q % p.groups) * p.cg;
     const uint32_t e0 = (uint32_t)(k * kChunk);           // chunk offset in the group, < 2^31
     const uint32_t sp = (uint32_t)p.spatial;
@@ -231,7 +334,14 @@ __device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k,
                 b = param<PARAM>(p.beta, c);
             }
             float f[8], o[8];
-            unpack8<X_FP16>(v[u], f);
+            if constexpr (RESCALED) {
+                unpack8<X_FP16>(load16<false>(xq + (int64_t)i * kVec), f);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    f[j] = __builtin_amdgcn_ldexpf(f[j], -st.shift);
+            } else {
+                unpack8<X_FP16>(v[u], f);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float t = __builtin_fmaf(f[j] - mean, a, b);
@@ -242,61 +352,150 @@ __device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k,
     }
 }
 
+template <bool X_FP16, int PARAM, int VPT>
+__device__ __forceinline__ void chunk_apply(const GnParams& p, int64_t q, int k, int nv,
+                                            const u32x4 (&v)[VPT], const GroupStats& st)
+{
+    if (__builtin_expect(st.shift == 0, 1))
+        chunk_apply_as<X_FP16, PARAM, VPT, false>(p, q, k, nv, v, st);
+    else
+        chunk_apply_as<X_FP16, PARAM, VPT, true>(p, q, k, nv, v, st);
+}
+
+// 1 / sqrt(var + eps) in the rescaled form, with the same floor: a group of
+// equal values has var_e = 0, and eps 2^-2e can underflow to 0 when e is
+// large; the floor keeps rstd finite for the group's zero deviations.
+__device__ __forceinline__ float rescaled_rstd(float var_s, float eps_s)
+{
+    return __builtin_amdgcn_rsqf(fmaxf(var_s + eps_s, 0x1p-126f));
+}
+
 // One chunk per group: statistics and output from one read.
 template <bool X_FP16, int PARAM>
 __global__ __launch_bounds__(kBlock) void gn_single_kernel(const GnParams p)
 {
-    __shared__ float red[2][kWaves];
+    __shared__ float red[5][kWaves];
     const int64_t q = blockIdx.x;
     const int nv = chunk_vectors<kVptMax>(p, 0);
     u32x4 v[kVptMax];
-    load_chunk<true>(p.x + q * p.group_size, nv, v);
+    const uint16_t* const base = p.x + q * p.group_size;
+    load_chunk<true>(base, nv, v);
     float mean, m2;
     chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
-    const float rstd = __builtin_amdgcn_rsqf(m2 / (float)p.group_size + p.eps);
-    chunk_apply<X_FP16, PARAM>(p, q, 0, nv, v, mean, rstd);
+    // in range, m2 / group_size + eps >= 2^-114: normal, as the hardware
+    // reciprocal square root needs
+    GroupStats st = {mean, __builtin_amdgcn_rsqf(m2 / (float)p.group_size + p.eps), 0};
+    if (__builtin_expect(!moments_in_range(m2, p.eps), 0)) {
+        int e;
+        float mean_s, m2_s;
+        chunk_moments_rescaled<X_FP16, kVptMax>(base, nv, red + 2, e, mean_s, m2_s);
+        const float eps_s = __builtin_amdgcn_ldexpf(p.eps, -2 * e);
+        if (eps_s <= kFltMax)
+            st = GroupStats{mean_s, rescaled_rstd(m2_s / (float)p.group_size, eps_s), e};
+        else    // the plain mean stands; the variance is nothing next to eps
+            st.rstd = rsqrt_full_range(m2 / (float)p.group_size + p.eps);
+    }
+    chunk_apply<X_FP16, PARAM>(p, q, 0, nv, v, st);
 }
 
 // Several chunks, pass 1: per-chunk mean and sum of squared deviations.
 template <bool X_FP16, int VPT>
 __global__ __launch_bounds__(kBlock) void gn_stats_kernel(const GnParams p)
 {
-    __shared__ float red[2][kWaves];
+    __shared__ float red[5][kWaves];
     const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
     const int nv = chunk_vectors<VPT>(p, k);
     u32x4 v[VPT];
-    load_chunk<false>(p.x + q * p.group_size + (int64_t)k * chunk_elems<VPT>(), nv, v);
+    const uint16_t* const base = p.x + q * p.group_size + (int64_t)k * chunk_elems<VPT>();
+    load_chunk<false>(base, nv, v);
     float mean, m2;
     chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
-    if (threadIdx.x == 0) {
-        float* out = p.partial + 2 * (q * p.chunks + k);
-        out[0] = mean;
-        out[1] = m2;
-    }
+    const f32x2 part = chunk_partial<X_FP16, VPT>(p, base, nv, mean, m2, red + 2);
+    if (threadIdx.x == 0)
+        *reinterpret_cast<f32x2*>(p.partial + 2 * (q * p.chunks + k)) = part;
 }
 
-// Group mean and 1/sqrt(var + eps) from the group's chunk partials `part`
-// ([chunks][2]), given this thread's first partial `first` (of chunk
-// threadIdx.x, if there is one).  Same order in every workgroup of the group:
-// thread sums over i = tid, tid + 256, ..., then the fixed-order workgroup
-// reduction through red0 and red1.
+// True when a partial is in the (mean, -sd) form of chunk_partial.
+__device__ __forceinline__ bool rescaled_form(float second) { return (__float_as_uint(second) >> 31) != 0; }
+
+// Partial (mean, m2 or -sd) of n elements as (mean, sd).
+__device__ __forceinline__ f32x2 mean_sd(f32x2 w, float n)
+{
+    return rescaled_form(w[1]) ? f32x2{w[0], -w[1]} : f32x2{w[0], __builtin_sqrtf(w[1] / n)};
+}
+
+// combine_partials for a group whose plain combine is out of range, or that
+// holds a partial in the (mean, -sd) form: with e the exponent of the largest
+// |mean_i| or sd_i, the group mean and variance of x * 2^-e from
+// sum n_i m_i 2^-e / N and sum n_i ((sd_i 2^-e)^2 + (m_i 2^-e - mean)^2) / N,
+// every term at most 1 in magnitude.  Three slots (red[0..2]).
 template <int VPT>
-__device__ __forceinline__ void combine_partials(const GnParams& p, const float* part,
-                                                 f32x2 first, float* red0, float* red1,
-                                                 float& mean, float& rstd)
+__device__ __forceinline__ GroupStats combine_rescaled(const GnParams& p, const float* part,
+                                                       f32x2 first, float (*red)[kWaves])
 {
     constexpr int64_t kChunk = chunk_elems<VPT>();
     const float last_n = (float)(p.group_size - (int64_t)(p.chunks - 1) * kChunk);
     const int i0 = threadIdx.x;
     const bool has0 = i0 < p.chunks;
     const float n0 = i0 == p.chunks - 1 ? last_n : (float)kChunk;
-    float s = has0 ? n0 * first[0] : 0.0f;
+    const f32x2 a0 = mean_sd(first, n0);
+    float mx = has0 ? fmaxf(fabsf(a0[0]), a0[1]) : 0.0f;
     for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
         const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
-        s = __builtin_fmaf(n_i, part[2 * i], s);
+        const f32x2 a = mean_sd(f32x2{part[2 * i], part[2 * i + 1]}, n_i);
+        mx = fmaxf(mx, fmaxf(fabsf(a[0]), a[1]));
     }
-    mean = block_sum<kWaves>(s, red0) / (float)p.group_size;
+    const int e = __builtin_amdgcn_frexp_expf(block_max<kWaves>(mx, red[0]));
+    float s = has0 ? n0 * __builtin_amdgcn_ldexpf(a0[0], -e) : 0.0f;
+    for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
+        const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
+        s = __builtin_fmaf(n_i, __builtin_amdgcn_ldexpf(part[2 * i], -e), s);
+    }
+    const float mean_s = block_sum<kWaves>(s, red[1]) / (float)p.group_size;
+    float v = 0.0f;
+    if (has0) {
+        const float sd = __builtin_amdgcn_ldexpf(a0[1], -e);
+        const float d = __builtin_amdgcn_ldexpf(a0[0], -e) - mean_s;
+        v = n0 * __builtin_fmaf(sd, sd, d * d);
+    }
+    for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
+        const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
+        const f32x2 a = mean_sd(f32x2{part[2 * i], part[2 * i + 1]}, n_i);
+        const float sd = __builtin_amdgcn_ldexpf(a[1], -e);
+        const float d = __builtin_amdgcn_ldexpf(a[0], -e) - mean_s;
+        v = __builtin_fmaf(n_i, __builtin_fmaf(sd, sd, d * d), v);
+    }
+    const float var_s = block_sum<kWaves>(v, red[2]) / (float)p.group_size;
+    const float eps_s = __builtin_amdgcn_ldexpf(p.eps, -2 * e);
+    if (eps_s <= kFltMax)
+        return GroupStats{mean_s, rescaled_rstd(var_s, eps_s), e};
+    return GroupStats{__builtin_amdgcn_ldexpf(mean_s, e), rsqrt_full_range(p.eps), 0};
+}
+
+// Group statistics from the group's chunk partials `part` ([chunks][2]),
+// given this thread's first partial `first` (of chunk threadIdx.x, if there
+// is one).  Same order in every workgroup of the group: thread sums over
+// i = tid, tid + 256, ..., then the fixed-order workgroup reduction through
+// red[0] and red[1].  A partial in the (mean, -sd) form turns the plain sum
+// into NaN, so that such a group, like one whose plain combine overflows,
+// takes combine_rescaled (slots red[2..4]).
+template <int VPT>
+__device__ __forceinline__ GroupStats combine_partials(const GnParams& p, const float* part,
+                                                       f32x2 first, float (*red)[kWaves])
+{
+    constexpr int64_t kChunk = chunk_elems<VPT>();
+    const float last_n = (float)(p.group_size - (int64_t)(p.chunks - 1) * kChunk);
+    const float nan = __builtin_nanf("");
+    const int i0 = threadIdx.x;
+    const bool has0 = i0 < p.chunks;
+    const float n0 = i0 == p.chunks - 1 ? last_n : (float)kChunk;
+    float s = has0 ? n0 * (rescaled_form(first[1]) ? nan : first[0]) : 0.0f;
+    for (int i = i0 + kBlock; i < p.chunks; i += kBlock) {
+        const float n_i = i == p.chunks - 1 ? last_n : (float)kChunk;
+        s = __builtin_fmaf(n_i, rescaled_form(part[2 * i + 1]) ? nan : part[2 * i], s);
+    }
+    const float mean = block_sum<kWaves>(s, red[0]) / (float)p.group_size;
     float m2 = 0.0f;
     if (has0) {
         const float d = first[0] - mean;
@@ -307,7 +506,14 @@ __device__ __forceinline__ void combine_partials(const GnParams& p, const float*
         const float d = part[2 * i] - mean;
         m2 += __builtin_fmaf(n_i * d, d, part[2 * i + 1]);
     }
-    rstd = __builtin_amdgcn_rsqf(block_sum<kWaves>(m2, red1) / (float)p.group_size + p.eps);
+    const float m2t = block_sum<kWaves>(m2, red[1]);
+    const float qv = m2t / (float)p.group_size + p.eps;
+    // a NaN mean makes m2t NaN too; a group of up to 2^31 elements can bring
+    // m2t / N below the normal range, which the hardware reciprocal square
+    // root does not take
+    if (__builtin_expect(moments_in_range(m2t, p.eps) && qv <= kFltMax && qv >= 0x1p-126f, 1))
+        return GroupStats{mean, __builtin_amdgcn_rsqf(qv), 0};
+    return combine_rescaled<VPT>(p, part, first, red + 2);
 }
 
 // Several chunks, pass 2: combine the group's partials, write the chunk.
@@ -315,7 +521,7 @@ template <bool X_FP16, int PARAM, int VPT>
 __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
 {
     constexpr int64_t kChunk = chunk_elems<VPT>();
-    __shared__ float red[2][kWaves];
+    __shared__ float red[5][kWaves];
     const int64_t q = blockIdx.x / p.chunks;
     const int k = (int)(blockIdx.x % p.chunks);
     const int nv = chunk_vectors<VPT>(p, k);
@@ -327,9 +533,8 @@ __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
         first = *reinterpret_cast<const f32x2*>(part + 2 * threadIdx.x);
     u32x4 v[VPT];
     load_chunk<true>(p.x + q * p.group_size + (int64_t)k * kChunk, nv, v);
-    float mean, rstd;
-    combine_partials<VPT>(p, part, first, red[0], red[1], mean, rstd);
-    chunk_apply<X_FP16, PARAM>(p, q, k, nv, v, mean, rstd);
+    const GroupStats st = combine_partials<VPT>(p, part, first, red);
+    chunk_apply<X_FP16, PARAM>(p, q, k, nv, v, st);
 }
 
 // Lagged schedule.  A chunk's word in the workspace holds its mean (low 32
@@ -339,9 +544,10 @@ __global__ __launch_bounds__(kBlock) void gn_apply_kernel(const GnParams p)
 constexpr uint64_t kEmpty = ~0ull;
 // Polls of an unpublished word (a few ms) before a workgroup reduces that
 // chunk itself.  Never reached in a lone call, where the chunks an output
-// waits for were reduced several hundred workgroups earlier.  The environment
-// variable QKR_GN_WAIT_POLLS overrides it (0: reduce at once), which makes
-// every waiter take the reduce-it-here path.
+// waits for were reduced several hundred workgroups earlier.  The library's
+// calls always use it; only the test entry point dit_group_norm_silu_polls
+// takes another count (0: reduce at once, which makes every waiter take the
+// reduce-it-here path).
 constexpr int kWaitPolls = 1 << 12;
 
 // Mark every chunk word of the call as not yet published.
@@ -359,25 +565,28 @@ __global__ __launch_bounds__(kBlock) void gn_clear_kernel(const GnParams p)
 // and in place, a reduction that read data the chunk's output had already
 // replaced never stands, since that output was written only after a word
 // was published.  Returns, in thread 0, the word that stands.
+// Slots: red[0..1] for the plain moments, red[2..4] for a rescaled chunk.
 template <bool X_FP16, bool STREAMED>
 __device__ __forceinline__ uint64_t reduce_and_publish(const GnParams& p, int64_t q, int k,
-                                                       float* red0, float* red1)
+                                                       float (*red)[kWaves])
 {
     constexpr int VPT = kVptMax;
     const int nv = chunk_vectors<VPT>(p, k);
     const uint16_t* const base = p.x + q * p.group_size + (int64_t)k * chunk_elems<VPT>();
     float mean, m2;
     if constexpr (STREAMED) {
-        chunk_moments_streamed<X_FP16, VPT>(base, nv, red0, red1, mean, m2);
+        chunk_moments_streamed<X_FP16, VPT>(base, nv, red[0], red[1], mean, m2);
     } else {
         u32x4 v[VPT];
         load_chunk<false>(base, nv, v);
-        chunk_moments<X_FP16>(v, nv, red0, red1, mean, m2);
+        chunk_moments<X_FP16>(v, nv, red[0], red[1], mean, m2);
     }
+    const f32x2 part = chunk_partial<X_FP16, VPT>(p, base, nv, mean, m2, red + 2);
     uint64_t stands = 0;
     if (threadIdx.x == 0) {
         uint64_t* const w = reinterpret_cast<uint64_t*>(p.partial) + q * p.chunks + k;
-        const uint64_t mine = (uint64_t)__float_as_uint(mean) | ((uint64_t)__float_as_uint(m2) << 32);
+        const uint64_t mine =
+            (uint64_t)__float_as_uint(part[0]) | ((uint64_t)__float_as_uint(part[1]) << 32);
         uint64_t expected = kEmpty;
         stands = __hip_atomic_compare_exchange_strong(w, &expected, mine, __ATOMIC_RELAXED,
                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
@@ -397,7 +606,7 @@ __global__ __launch_bounds__(kBlock) void gn_lagged_kernel(const GnParams p)
 {
     constexpr int VPT = kVptMax;
     constexpr int64_t kChunk = chunk_elems<VPT>();
-    __shared__ float red[4][kWaves];
+    __shared__ float red[10][kWaves];     // [0..4] chunk reductions, [5..9] the combine
     __shared__ int missing;
     __shared__ uint64_t helped;
     const int64_t b = blockIdx.x;
@@ -413,7 +622,7 @@ __global__ __launch_bounds__(kBlock) void gn_lagged_kernel(const GnParams p)
         load_chunk<true>(p.x + qo * p.group_size + (int64_t)ko * kChunk, nvo, w);
     }
     if (b < p.total)
-        reduce_and_publish<X_FP16, false>(p, b / p.chunks, (int)(b % p.chunks), red[0], red[1]);
+        reduce_and_publish<X_FP16, false>(p, b / p.chunks, (int)(b % p.chunks), red);
     if (!out)
         return;
 
@@ -442,7 +651,7 @@ __global__ __launch_bounds__(kBlock) void gn_lagged_kernel(const GnParams p)
             const int m = missing;
             if (m == kBlock)
                 break;
-            const uint64_t stands = reduce_and_publish<X_FP16, true>(p, qo, m, red[0], red[1]);
+            const uint64_t stands = reduce_and_publish<X_FP16, true>(p, qo, m, red);
             if (i == 0)
                 helped = stands;
             __syncthreads();
@@ -454,9 +663,8 @@ __global__ __launch_bounds__(kBlock) void gn_lagged_kernel(const GnParams p)
     const f32x2 first = watch ? f32x2{__uint_as_float((uint32_t)bits),
                                       __uint_as_float((uint32_t)(bits >> 32))}
                               : f32x2{0.0f, 0.0f};
-    float mean, rstd;
-    combine_partials<VPT>(p, p.partial + 2 * qo * p.chunks, first, red[2], red[3], mean, rstd);
-    chunk_apply<X_FP16, PARAM>(p, qo, ko, nvo, w, mean, rstd);
+    const GroupStats st = combine_partials<VPT>(p, p.partial + 2 * qo * p.chunks, first, red + 5);
+    chunk_apply<X_FP16, PARAM>(p, qo, ko, nvo, w, st);
 }
 
 using GnFn = void (*)(GnParams);
@@ -591,10 +799,13 @@ extern "C" int32_t dit_group_norm_silu_schedule(int64_t n, int32_t channels, int
     return schedule_for(pairs, chunks, vpt, &lag);
 }
 
-extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels,
-                                   int64_t spatial, int32_t groups, const void* gamma,
-                                   const void* beta, int32_t param_dtype, float eps, int32_t dtype,
-                                   void* workspace, int64_t workspace_bytes, void* stream)
+namespace {
+
+// The call, with the lagged schedule's polls per unpublished word.
+int run_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int64_t spatial,
+                        int32_t groups, const void* gamma, const void* beta, int32_t param_dtype,
+                        float eps, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                        void* stream, int32_t wait_polls)
 {
     if (dtype < QKR_BF16 || dtype > QKR_FP32 || param_dtype < QKR_BF16 || param_dtype > QKR_FP32)
         return QKR_ERR_ARG;
@@ -642,11 +853,7 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
     p.chunks = (int32_t)chunks;
     p.eps = eps;
     p.total = pairs * chunks;
-    p.wait_polls = kWaitPolls;
-    if (const char* env = getenv("QKR_GN_WAIT_POLLS")) {
-        const long v = strtol(env, nullptr, 10);
-        p.wait_polls = v < 0 ? 0 : v > kWaitPolls ? kWaitPolls : (int32_t)v;
-    }
+    p.wait_polls = wait_polls;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool xf = dtype == QKR_FP16;
 
@@ -672,4 +879,30 @@ extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t ch
         pick_pair<2>(xf, param_dtype, &stats, &apply);
     const int r = launch(stats, pairs * chunks, p, s);
     return r == QKR_OK ? launch(apply, pairs * chunks, p, s) : r;
+}
+
+}  // namespace
+
+extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels,
+                                   int64_t spatial, int32_t groups, const void* gamma,
+                                   const void* beta, int32_t param_dtype, float eps, int32_t dtype,
+                                   void* workspace, int64_t workspace_bytes, void* stream)
+{
+    return run_group_norm_silu(x, y, n, channels, spatial, groups, gamma, beta, param_dtype, eps,
+                               dtype, workspace, workspace_bytes, stream, kWaitPolls);
+}
+
+// Test entry point (declared in the tests' own header, not the library's):
+// dit_group_norm_silu with the lagged schedule's polls per unpublished word
+// set by the caller, 0 .. 4096 (QKR_ERR_ARG otherwise).
+extern "C" int dit_group_norm_silu_polls(const void* x, void* y, int64_t n, int32_t channels,
+                                         int64_t spatial, int32_t groups, const void* gamma,
+                                         const void* beta, int32_t param_dtype, float eps,
+                                         int32_t dtype, void* workspace, int64_t workspace_bytes,
+                                         void* stream, int32_t wait_polls)
+{
+    if (wait_polls < 0 || wait_polls > kWaitPolls)
+        return QKR_ERR_ARG;
+    return run_group_norm_silu(x, y, n, channels, spatial, groups, gamma, beta, param_dtype, eps,
+                               dtype, workspace, workspace_bytes, stream, wait_polls);
 }

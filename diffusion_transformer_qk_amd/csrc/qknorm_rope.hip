@@ -83,6 +83,20 @@ __device__ __forceinline__ float head_sum(float v)
     return v;
 }
 
+// Largest value over the L lanes of one head (the butterfly of head_sum).
+template <int L>
+__device__ __forceinline__ float head_max(float v)
+{
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    if constexpr (L >= 16)
+        v = fmaxf(v, dpp<0x140>(v));
+    if constexpr (L == 32)
+        v = fmaxf(v, lane_xor16(v));
+    return v;
+}
+
 // Value held by the lane L/2 positions away within the head (the lane whose
 // dimensions are D/2 away).
 template <int L>
@@ -141,19 +155,56 @@ __device__ __forceinline__ void rotation_coeffs(const float g[8], const float gp
     }
 }
 
-// One head's slice in this lane: 8 elements in, 8 rotated, normalised out.
-template <int D, int STYLE, bool X_FP16>
-__device__ __forceinline__ u32x4 head_math(const u32x4 v, const float A[8], const float B[8], float eps)
+// Sums of squares at or above this keep full fp32 precision (their largest
+// terms are normal numbers); below it, subnormal squares lose bits, which
+// only matters when eps is below it too.
+constexpr float kTinySum = 0x1p-100f;
+
+// Whether the fp32 sum of squares ss (of q = ss / D + eps) gives the head's
+// scale exactly enough: q finite, and ss either clear of the subnormal range
+// or swamped by eps.  False for a sum that overflowed (a head of 16-bit
+// values whose RMS exceeds about 1.6e18) and for NaN.  When true, q is at
+// least 2^-108, a normal number, as the hardware reciprocal square root needs.
+__device__ __forceinline__ bool sum_in_range(float ss, float q, float eps)
 {
-    constexpr int L = D / kVec;
-    float f[8];
-    unpack8<X_FP16>(v, f);
+    return q <= 0x1.fffffep127f && (ss >= kTinySum || eps >= kTinySum);
+}
+
+// The head's 1 / sqrt(mean(x^2) + eps) when the plain fp32 sum is out of
+// range: with e the binary exponent of the head's largest |x|, sum the
+// squares of x * 2^-e (an exact power-of-two scaling, all terms <= 1) and use
+// 1 / sqrt(mean((x 2^-e)^2) + eps 2^-2e), which multiplies x * 2^-e: f is
+// rescaled in place.  If eps 2^-2e overflows, mean(x^2) is below eps by more
+// than 2^128 and 1 / sqrt(eps) is the answer, for f as it is.
+template <int L, int D>
+__device__ __forceinline__ float rescaled_rsqrt(float f[8], float eps)
+{
+    float m = fabsf(f[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        m = fmaxf(m, fabsf(f[i]));
+    const int e = __builtin_amdgcn_frexp_expf(head_max<L>(m));
+    const float eps_s = __builtin_amdgcn_ldexpf(eps, -2 * e);
+    if (!(eps_s <= 0x1.fffffep127f))
+        return rsqrt_full_range(eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        f[i] = __builtin_amdgcn_ldexpf(f[i], -e);
     float ss = f[0] * f[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i)
         ss = __builtin_fmaf(f[i], f[i], ss);
-    ss = head_sum<L>(ss);
-    const float r = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, 1.0f / D, eps));
+    // the sum is at least 1/4 unless the head is all zeros; then it is eps,
+    // which may be subnormal
+    return rsqrt_full_range(__builtin_fmaf(head_sum<L>(ss), 1.0f / D, eps_s));
+}
+
+// Rotated, normalised output of one head's slice in this lane: y = f * r,
+// then o = y A + y_partner B, rounded to the data type.
+template <int D, int STYLE, bool X_FP16>
+__device__ __forceinline__ u32x4 head_out(const float f[8], float r, const float A[8], const float B[8])
+{
+    constexpr int L = D / kVec;
     float y[8], yp[8], o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -165,6 +216,65 @@ __device__ __forceinline__ u32x4 head_math(const u32x4 v, const float A[8], cons
     for (int i = 0; i < 8; ++i)
         o[i] = __builtin_fmaf(y[i], A[i], yp[i] * B[i]);
     return pack8<X_FP16>(o);
+}
+
+// One head's slice in this lane: 8 elements in, 8 rotated, normalised out.
+// `in_range` (the same in every lane of a head) is false when the head's
+// plain fp32 sum of squares is out of range; its output is then not valid
+// and the head goes through fix_heads instead.
+template <int D, int STYLE, bool X_FP16>
+__device__ __forceinline__ u32x4 head_math(const u32x4 v, const float A[8], const float B[8], float eps,
+                                           bool& in_range)
+{
+    constexpr int L = D / kVec;
+    float f[8];
+    unpack8<X_FP16>(v, f);
+    float ss = f[0] * f[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i)
+        ss = __builtin_fmaf(f[i], f[i], ss);
+    ss = head_sum<L>(ss);
+    const float q = __builtin_fmaf(ss, 1.0f / D, eps);
+    in_range = sum_in_range(ss, q, eps);
+    return head_out<D, STYLE, X_FP16>(f, __builtin_amdgcn_rsqf(q), A, B);
+}
+
+// The heads of iterations `redo` (a bit per iteration u of the chunk at h0)
+// whose plain sum of squares was out of range: they were not written, so
+// each is read again and normalised through rescaled_rsqrt.  Kept out of the
+// unrolled loop so that the registers of the in-flight loads are not charged
+// for this rarely taken path.  Every lane of a head has the same bits.
+template <int D, int STYLE, bool PER_HEAD, bool COS_BF16, bool X_FP16, int U>
+__device__ __forceinline__ void fix_heads(const Params& p, uint16_t* row, int64_t t, int h0, int hs,
+                                          int d0, uint32_t redo, const float g[8], const float gp[8],
+                                          const float A[8], const float B[8])
+{
+    constexpr int L = D / kVec;
+    constexpr int HPI = kWave / L;
+#pragma unroll 1
+    for (int u = 0; u < U; ++u) {
+        if ((redo >> u) & 1u) {
+            const int h = h0 + u * HPI + hs;
+            float f[8];
+            unpack8<X_FP16>(load16<false>(row + h * D + d0), f);
+            float Ah[8], Bh[8];
+            if constexpr (PER_HEAD) {
+                const int64_t idx = (t * p.heads + h) * D + d0;
+                float c[8], sn[8];
+                load_table8<COS_BF16>(p.cos, idx, c);
+                load_table8<COS_BF16>(p.sin, idx, sn);
+                rotation_coeffs<D, STYLE>(g, gp, c, sn, d0, Ah, Bh);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    Ah[i] = A[i];
+                    Bh[i] = B[i];
+                }
+            }
+            const float r = rescaled_rsqrt<L, D>(f, p.eps);
+            store16<false>(row + h * D + d0, head_out<D, STYLE, X_FP16>(f, r, Ah, Bh));
+        }
+    }
 }
 
 // Issue the loads of U head iterations starting at head h0 (plus, for the
@@ -298,23 +408,32 @@ __global__ __launch_bounds__(WAVES * kWave) void qknorm_rope_kernel(const Params
     }
 
     for (int h0 = 0;;) {
+        uint32_t redo = 0;     // bit u: head iteration u is out of range, not stored
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int h = h0 + u * HPI + hs;
             u32x4 out;
+            bool in_range;
             if constexpr (PER_HEAD) {
                 constexpr int NV = table_vecs<COS_BF16>();
                 float c[8], sn[8], Ah[8], Bh[8];
                 widen_table<COS_BF16>(&tw[2 * u * NV], c);
                 widen_table<COS_BF16>(&tw[(2 * u + 1) * NV], sn);
                 rotation_coeffs<D, STYLE>(g, gp, c, sn, d0, Ah, Bh);
-                out = head_math<D, STYLE, X_FP16>(v[u], Ah, Bh, p.eps);
+                out = head_math<D, STYLE, X_FP16>(v[u], Ah, Bh, p.eps, in_range);
             } else {
-                out = head_math<D, STYLE, X_FP16>(v[u], A, B, p.eps);
+                out = head_math<D, STYLE, X_FP16>(v[u], A, B, p.eps, in_range);
             }
-            if (h < H)
-                store16<(NT & 2) != 0>(row + h * D + d0, out);
+            if (h < H) {
+                if (__builtin_expect(in_range, 1))
+                    store16<(NT & 2) != 0>(row + h * D + d0, out);
+                else
+                    redo |= 1u << u;
+            }
         }
+        if (__builtin_expect(redo != 0, 0))
+            fix_heads<D, STYLE, PER_HEAD, COS_BF16, X_FP16, U>(p, row, t, h0, hs, d0, redo, g, gp,
+                                                             A, B);
         h0 += HPI * U;
         if (h0 >= H)
             break;

@@ -15,7 +15,11 @@
  *     y[c] = (x[c] - mean) / sqrt(var + eps) * (1 + scale[b, c]) + shift[b, c]
  *
  * Math is fp32 (two passes over the row held in registers); y is rounded
- * once, to nearest even, to x's dtype.
+ * once, to nearest even, to x's dtype.  Any finite input is normalised
+ * correctly: a row whose plain fp32 sums would overflow (bf16 values beyond
+ * about 1e17) or sink into the subnormal range while eps is below 2^-100 is
+ * reduced again on x * 2^-e, e the binary exponent of its largest magnitude
+ * (an exact rescaling), and normalised in that scale.
  *
  * Pointers are DEVICE pointers owned by the caller; the library allocates,
  * frees and synchronises nothing.  y may be x itself (in place) or a buffer

@@ -21,7 +21,11 @@
  * squared deviations per chunk) go to a caller-owned workspace; the chunks
  * are then combined exactly as a two-level reduction (Chan et al.).  Every
  * schedule combines them in the same order, so a shape's output bits do not
- * depend on which schedule runs it (dit_group_norm_silu_schedule).
+ * depend on which schedule runs it (dit_group_norm_silu_schedule).  Any
+ * finite input is normalised correctly: a chunk or group whose plain fp32
+ * sums would overflow (bf16 values beyond about 1e17) or sink into the
+ * subnormal range while eps is below 2^-100 is reduced again on x * 2^-e,
+ * e the binary exponent of its largest magnitude (an exact rescaling).
  *
  * Pointers are DEVICE pointers owned by the caller; the library allocates,
  * frees and synchronises nothing.  y may be x itself or a buffer that does
@@ -61,10 +65,7 @@ int64_t dit_group_norm_silu_workspace_size(int64_t n, int32_t channels, int64_t 
  *      that finds a word still unpublished after a few ms of polling reduces
  *      that chunk itself; the first word published for a chunk stands
  *      (compare-and-swap), so the call ends whatever order its workgroups
- *      start in, also beside other work.  The environment variable
- *      QKR_GN_WAIT_POLLS (read per call; default and maximum 4096) sets the
- *      polls before that; 0 makes every waiter reduce at once, which tests
- *      use to exercise that path.  A small kernel first marks the
+ *      start in, also beside other work.  A small kernel first marks the
  *      workspace's words unpublished;
  *   2  two passes: a statistics kernel, then an apply kernel that re-reads x.
  */

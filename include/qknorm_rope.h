@@ -13,7 +13,11 @@
  *                                                      rotate-half (i, i + head_dim/2)
  *
  * written back in place over Q and K, rounded once (round to nearest even) to
- * the tensor's dtype; math is fp32 inside.  The cos/sin row of token t is
+ * the tensor's dtype; math is fp32 inside.  Any finite input is normalised
+ * correctly: a head whose fp32 sum of squares would overflow (bf16 values
+ * with an RMS beyond about 1.6e18) or sink into the subnormal range while
+ * eps is below 2^-100 is summed again on x * 2^-e, e the binary exponent of
+ * its largest |x| (an exact rescaling).  The cos/sin row of token t is
  * either shared by all heads ([tokens, head_dim], "shared") or given per head
  * ([tokens, heads, head_dim], "per-head"); row (t, h) serves Q head h and K
  * head h.  The V slice of a fused buffer is never read or written.

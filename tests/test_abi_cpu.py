@@ -313,3 +313,29 @@ def test_group_norm_schedule_rejects_what_the_call_rejects():
     lib = qkr.load_library()
     assert lib.dit_group_norm_silu_schedule(1, 8, 64, 2, None) == 0      # the size out-pointer is optional
 
+
+
+def test_group_norm_test_hook_is_outside_the_public_headers():
+    """dit_group_norm_silu_polls is exported for the tests only: declared in
+    tests/c_abi/gn_test_hooks.h, not under include/, and it rejects a poll
+    count outside 0..4096 before any HIP call."""
+    from tests import gn_hooks
+
+    assert "dit_group_norm_silu_polls" not in declared_functions()
+    hooks = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "gn_test_hooks.h")
+    with open(hooks) as f:
+        assert "int dit_group_norm_silu_polls(" in f.read()
+    for polls in (-1, gn_hooks.MAX_POLLS + 1):
+        assert gn_hooks.polls_raw(A, A + (1 << 30), 1, 64, 64, 8, A, A, b.QKR_FP32, 1e-6,
+                                  b.QKR_BF16, 0, 0, 0, polls) == b.QKR_ERR_ARG
+
+
+def test_library_reads_no_environment():
+    """The shipped library's behaviour depends on its arguments only: it
+    imports no environment-reading function."""
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--undefined-only", qkr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert not names & {"getenv", "secure_getenv", "__secure_getenv"}, names & {"getenv"}

@@ -348,3 +348,70 @@ def test_every_kernel_instantiation(dtype, mod):
                            "hidden %d rows %d" % (hidden, rows))
     assert hit == {(v, f, s) for v in range(2, 17, 2) for f in (True, False)
                    for s in (True, False)}
+
+
+# ----------------------------------------------------------------------------- large and tiny finite values
+
+
+def _rows_with_peaks(rng, rows, hidden, peaks):
+    """fp64 [rows, hidden]: N(0.5, 1) rows rescaled so that each row's largest
+    |x| is one of `peaks`, cycling over the rows."""
+    raw = rng.standard_normal((rows, hidden)) + 0.5
+    raw /= np.abs(raw).max(axis=1, keepdims=True)
+    return raw * np.asarray(peaks, dtype=np.float64)[np.arange(rows) % len(peaks)][:, None]
+
+
+def _special_rows(raw, rng):
+    """A constant row at 3e38 (zero variance), an O(1) row with one element
+    at 3.3e38, and a row alternating +-3.3e38."""
+    hidden = raw.shape[1]
+    raw[1] = 3e38
+    raw[2] = rng.standard_normal(hidden)
+    raw[2, 5] = 3.3e38
+    raw[3] = 3.3e38 * np.where(np.arange(hidden) % 2 == 0, 1.0, -1.0)
+    return raw
+
+
+@pytest.mark.parametrize("rows,hidden", [(64, 5120), (70, 1000), (8200, 1024)])
+def test_large_finite_bf16_rows(rows, hidden):
+    """bf16 rows whose fp32 sums or squared deviations overflow (largest |x|
+    1e18, 1e30, 3e38) between O(1) rows, in the one-row schedule (with a full
+    and a ragged row width) and in the 4-row staging schedule; plus a constant
+    row of 3e38, a spike and an alternating +-3.3e38 row.  Every element
+    against the oracle."""
+    rng = np.random.default_rng(800 + rows)
+    raw = _special_rows(_rows_with_peaks(rng, rows, hidden, [1.0, 1e18, 1e30, 3e38, 7.0]), rng)
+    x = torch.from_numpy(raw.astype(np.float32)).to(torch.bfloat16)
+    assert torch.isfinite(x.float()).all()
+    sc = torch.from_numpy((0.5 * rng.standard_normal((1, hidden))).astype(np.float32))
+    sh = torch.from_numpy((0.5 * rng.standard_normal((1, hidden))).astype(np.float32))
+    out = run(x, sc, sh)
+    y, n = oracle_rows(x, "bf16", sc, sh, rows, wl.EPS)
+    got = _decode(out, "bf16")
+    m = check_rows(got, y, n, sc, sh, rows, 0, "bf16", "large rows %dx%d" % (rows, hidden))
+    # the constant row is the shift alone (up to its rounding)
+    assert np.all(got.reshape(rows, hidden)[1] == oracle.round_to(_mod_values(sh)[0], "bf16"))
+    inplace = run(x, sc, sh, inplace=True)
+    assert torch.equal(inplace.view(torch.int16), out.view(torch.int16))
+    print("large finite bf16 rows", rows, hidden, "max_abs", m)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1e-38, 1.4e-45])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_tiny_rows_and_tiny_eps(eps, dtype):
+    """Rows of tiny values (down to bf16 subnormals near 1e-40, fp16
+    subnormals near 1e-7) with eps down to the smallest fp32 subnormal; an
+    all-zero row.  Every element against the oracle."""
+    rows, hidden = 48, 2048
+    rng = np.random.default_rng(810)
+    peaks = ([1.0, 1e-12, 1e-20, 1e-30, 1e-38, 1e-40] if dtype == "bf16"
+             else [1.0, 1e-3, 1e-5, 3e-7, 5.0])
+    raw = _rows_with_peaks(rng, rows, hidden, peaks)
+    raw[0] = 0.0
+    x = torch.from_numpy(raw.astype(np.float32)).to(wl.DTYPES[dtype])
+    sc = torch.from_numpy((0.5 * rng.standard_normal((1, hidden))).astype(np.float32))
+    sh = torch.from_numpy((0.5 * rng.standard_normal((1, hidden))).astype(np.float32))
+    out = run(x, sc, sh, eps=eps)
+    y, n = oracle_rows(x, dtype, sc, sh, rows, eps)
+    m = check_rows(_decode(out, dtype), y, n, sc, sh, rows, 0, dtype, "tiny rows eps %g" % eps)
+    print("tiny rows", dtype, "eps", eps, "max_abs", m)

@@ -16,6 +16,7 @@ import torch
 import diffusion_transformer_qk_amd as qkr
 import oracle
 import workloads as wl
+from tests import gn_hooks
 from tests.gpu_common import decode as _decode, same_bits, ulp as _ulp
 
 pytestmark = pytest.mark.gpu
@@ -422,22 +423,22 @@ def test_lagged_in_place_and_any_workspace_contents():
     ((1, 128, 1024 * 1024, 32), "bf16", "fp32"),     # VAE out: 256 chunks per group
     ((8, 512, 16392, 32), "fp16", "bf16"),           # channel boundaries inside chunks
 ])
-def test_lagged_waiters_that_reduce_chunks_themselves(monkeypatch, shape, dtype, param):
-    """With no polling allowed (QKR_GN_WAIT_POLLS=0) every workgroup whose
-    group is not complete at its first look reduces the missing chunks
-    itself, racing their own workgroups; the first word published stands.
-    Out of place and in place, the bits equal the default call's."""
+def test_lagged_waiters_that_reduce_chunks_themselves(shape, dtype, param):
+    """With no polling allowed (the test entry point with 0 polls) every
+    workgroup whose group is not complete at its first look reduces the
+    missing chunks itself, racing their own workgroups; the first word
+    published stands.  Out of place and in place, the bits equal the library
+    call's."""
     n, channels, spatial, groups = shape
     x, g, b = _lagged_inputs(8300, dtype, param, shape=shape)
     xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
     want = qkr.group_norm_silu(xd, gd, bd, groups)
     torch.cuda.synchronize()
-    monkeypatch.setenv("QKR_GN_WAIT_POLLS", "0")
     for _ in range(3):
-        got = qkr.group_norm_silu(xd, gd, bd, groups)
+        got = gn_hooks.group_norm_silu_polls(xd, gd, bd, groups, 0)
         xi = xd.clone()
         torch.cuda.synchronize()
-        qkr.group_norm_silu(xi, gd, bd, groups, out=xi)
+        gn_hooks.group_norm_silu_polls(xi, gd, bd, groups, 0, out=xi)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), want.view(torch.int16))
         assert torch.equal(xi.view(torch.int16), want.view(torch.int16))
@@ -489,3 +490,150 @@ def test_lagged_calls_on_concurrent_streams():
     for (_, _, _, alone, _), out in zip(cases, outs):
         assert torch.equal(out.view(torch.int16), alone.view(torch.int16))
 
+
+
+# ----------------------------------------------------------------------------- large and tiny finite values
+
+
+def _groups_with_peaks(rng, n, channels, spatial, groups, peaks, chunk_peaks=None):
+    """fp64 [n, channels, spatial]: each channel N(b_c, 1), each group rescaled
+    so its largest |x| is one of `peaks` (cycling over the groups); with
+    `chunk_peaks`, the group's elements are rescaled in runs of 16384 instead
+    (chunks of different magnitude inside one group)."""
+    raw = rng.standard_normal((n, channels, spatial)) + rng.standard_normal(channels)[None, :, None]
+    flat = raw.reshape(n * groups, -1)
+    flat /= np.abs(flat).max(axis=1, keepdims=True)
+    peaks = np.asarray(peaks, dtype=np.float64)
+    flat *= peaks[np.arange(n * groups) % len(peaks)][:, None]
+    if chunk_peaks is not None:
+        cp = np.asarray(chunk_peaks, dtype=np.float64)
+        run_of = np.arange(flat.shape[1]) // 16384
+        flat *= cp[run_of % len(cp)][None, :]
+    return raw
+
+
+def _gn_case(raw, dtype, param, seed):
+    x = torch.from_numpy(raw.astype(np.float32)).to(wl.DTYPES[dtype])
+    assert torch.isfinite(x.float()).all()
+    rng = np.random.default_rng(seed)
+    c = raw.shape[1]
+    g = torch.from_numpy((1 + 0.1 * rng.standard_normal(c)).astype(np.float32))
+    b = torch.from_numpy((0.1 * rng.standard_normal(c)).astype(np.float32))
+    if param != "fp32":
+        g, b = g.to(wl.DTYPES[param]), b.to(wl.DTYPES[param])
+    return x, g, b
+
+
+@pytest.mark.parametrize("shape,schedule", [
+    ((2, 64, 64, 8), "one_read"),              # groups of 512: one chunk
+    ((1, 64, 4096, 8), "two_pass"),            # 8 chunks of 4096 per group
+    ((4, 96, 2048, 6), "two_pass"),            # 8 chunks of 4096 per group
+    (LAGGED, "lagged"),                        # 16 chunks of 16384 per group
+])
+def test_large_finite_bf16_groups(shape, schedule):
+    """bf16 groups whose fp32 chunk sums or squared deviations overflow
+    (largest |x| 1e18, 1e30, 3e38) between O(1) groups, in each schedule;
+    plus a constant group of 3e38 (zero variance) and a group of O(1) values
+    with one element at 3.3e38.  Every group against the oracle."""
+    n, channels, spatial, groups = shape
+    assert qkr.group_norm_silu_schedule(n, channels, spatial, groups)[0] == schedule
+    rng = np.random.default_rng(900 + spatial)
+    raw = _groups_with_peaks(rng, n, channels, spatial, groups, [1.0, 1e18, 1e30, 3e38, 4.0])
+    flat = raw.reshape(n * groups, -1)
+    flat[1] = 3e38
+    flat[2] = rng.standard_normal(flat.shape[1])
+    flat[2, 77] = 3.3e38
+    x, g, b = _gn_case(raw, "bf16", "fp32", 901)
+    out = run(x, g, b, groups)
+    gsize = channels // groups * spatial
+    ref = oracle_groups(x, "bf16", channels, spatial, groups, g, b, wl.EPS)
+    m = check_groups(_decode(out, "bf16"), ref, gsize, "bf16", "large groups %s" % (shape,))
+    inplace = run(x, g, b, groups, inplace=True)
+    assert torch.equal(inplace.view(torch.int16), out.view(torch.int16))
+    print("large finite bf16 groups", shape, schedule, "max_abs", m)
+
+
+@pytest.mark.parametrize("schedule_shape", [(1, 64, 4096, 2), LAGGED])
+def test_groups_mixing_chunk_magnitudes(schedule_shape):
+    """Groups whose chunks differ in magnitude (runs of 16384 elements at
+    1, 1e30, 3e38 and 1e-3 of the group's peak): some chunk partials take the
+    rescaled (mean, -sd) form and the group's combine goes rescaled too.
+    Every group against the oracle; the lagged schedule's forced helpers give
+    the same bits."""
+    n, channels, spatial, groups = schedule_shape
+    rng = np.random.default_rng(910)
+    raw = _groups_with_peaks(rng, n, channels, spatial, groups, [1.0, 3e38],
+                             chunk_peaks=[1.0, 1e-30, 1.0, 1e-8])
+    x, g, b = _gn_case(raw, "bf16", "fp32", 911)
+    out = run(x, g, b, groups)
+    gsize = channels // groups * spatial
+    ref = oracle_groups(x, "bf16", channels, spatial, groups, g, b, wl.EPS)
+    m = check_groups(_decode(out, "bf16"), ref, gsize, "bf16", "mixed chunks")
+    if qkr.group_norm_silu_schedule(n, channels, spatial, groups)[0] == "lagged":
+        xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+        helped = gn_hooks.group_norm_silu_polls(xd, gd, bd, groups, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(helped.cpu().view(torch.int16), out.view(torch.int16))
+    print("mixed chunk magnitudes", schedule_shape, "max_abs", m)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1e-38, 1.4e-45])
+@pytest.mark.parametrize("dtype,shape", [("bf16", (2, 64, 64, 8)), ("bf16", (1, 64, 4096, 8)),
+                                         ("fp16", (1, 64, 4096, 8))])
+def test_tiny_groups_and_tiny_eps(eps, dtype, shape):
+    """Groups of tiny values (down to bf16 subnormals near 1e-40, fp16 ones
+    near 1e-7) and an all-zero group, with eps down to the smallest fp32
+    subnormal.  Every group against the oracle."""
+    n, channels, spatial, groups = shape
+    rng = np.random.default_rng(920)
+    peaks = ([1.0, 1e-12, 1e-20, 1e-30, 1e-38, 1e-40] if dtype == "bf16"
+             else [1.0, 1e-3, 1e-5, 3e-7])
+    raw = _groups_with_peaks(rng, n, channels, spatial, groups, peaks)
+    raw.reshape(n * groups, -1)[0] = 0.0
+    x, g, b = _gn_case(raw, dtype, "fp32", 921)
+    out = run(x, g, b, groups, eps=eps)
+    gsize = channels // groups * spatial
+    ref = oracle_groups(x, dtype, channels, spatial, groups, g, b, eps)
+    m = check_groups(_decode(out, dtype), ref, gsize, dtype, "tiny groups eps %g" % eps)
+    print("tiny groups", dtype, shape, "eps", eps, "max_abs", m)
+
+
+@pytest.mark.parametrize("as_int", [False, True])
+def test_binding_allocates_on_the_launch_stream(monkeypatch, as_int):
+    """Called with a launch stream other than the current one (a torch
+    stream, or its raw handle), the workspace and output the binding
+    allocates belong to the launch stream: the caching allocator then reuses
+    their memory only in that stream's order, never for work the current
+    stream queues while the call may still run.  The launch stream is held
+    back by a spin kernel, the current stream allocates and fills memory of
+    the workspace's size right after the call, and the output still equals
+    the same call on one stream."""
+    n, channels, spatial, groups = LAGGED
+    x, g, b = _lagged_inputs(8600)
+    xd, gd, bd = x.to(DEV), g.to(DEV), b.to(DEV)
+    want = qkr.group_norm_silu(xd, gd, bd, groups)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    seen = []
+    real_empty, real_like = torch.empty, torch.empty_like
+
+    def empty(*a, **kw):
+        seen.append(torch.cuda.current_stream().cuda_stream)
+        return real_empty(*a, **kw)
+
+    def empty_like(*a, **kw):
+        seen.append(torch.cuda.current_stream().cuda_stream)
+        return real_like(*a, **kw)
+
+    need = qkr.group_norm_silu_workspace_size(n, channels, spatial, groups)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    monkeypatch.setattr(torch, "empty", empty)
+    monkeypatch.setattr(torch, "empty_like", empty_like)
+    got = qkr.group_norm_silu(xd, gd, bd, groups, stream=side.cuda_stream if as_int else side)
+    monkeypatch.undo()
+    junk = [torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    torch.cuda.synchronize()
+    assert len(seen) == 2 and set(seen) == {side.cuda_stream}, seen
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    del junk
