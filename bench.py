@@ -21,12 +21,19 @@ sample of the same workload.
   python bench.py --op eager_chain [--workload flux|headline|mid] [--dtype bf16|fp16]
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
                   [--layout shared|per_head] [--style interleaved|rotate_half]
-                  [--dtype bf16|fp16] [--flush] [--graph] [--no-cpu-baseline] [--calib-copy]
+                  [--dtype bf16|fp16] [--flush [--flush-mode clean|dirty]] [--graph]
+                  [--no-cpu-baseline] [--calib-copy]
+
+  python bench.py --op floor [--workload headline]
 
 Other workloads (tiny, mid, flux, large) are reported the same way; with
---flush a 1 GiB buffer is rewritten before every timed call (outside that
-call's event bracket) so that inputs smaller than the 256 MB Infinity Cache
-come from HBM, and ``value`` then uses the per-call event times.
+--flush the caches are evicted before every timed call (outside that call's
+event bracket; by default by reading a 1 GiB buffer, which leaves clean
+lines, or with --flush-mode dirty by writing one) so that inputs smaller than
+the 256 MB Infinity Cache come from HBM, and ``value`` then uses the per-call
+event times.  ``pct_of_peak`` uses the mean call time, ``pct_of_peak_median``
+the median.  --op floor times the pass beside no-arithmetic probes of its
+access pattern (bench_floor.hip).
 """
 from __future__ import annotations
 
@@ -96,7 +103,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--op", default="qknorm_rope",
                     choices=["qknorm_rope", "fuse_scale_shift", "group_norm_silu",
-                             "eager_chain"])
+                             "eager_chain", "floor"])
     ap.add_argument("--workload", default=None)
     ap.add_argument("--mod-dtype", default="fp32", choices=["fp32", "bf16", "fp16"])
     ap.add_argument("--inplace", action="store_true", help="AdaLN, group norm: write y over x")
@@ -105,7 +112,10 @@ def parse():
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
     ap.add_argument("--cos-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--flush", action="store_true",
-                    help="rewrite 1 GiB before each timed call (cache-cold inputs)")
+                    help="evict the caches before each timed call (cache-cold inputs)")
+    ap.add_argument("--flush-mode", default="clean", choices=["clean", "dirty"],
+                    help="clean: read a 1 GiB buffer (leaves clean lines); dirty: write 1 GiB "
+                         "(leaves dirty lines whose write-back may land in the timed call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU-oracle sample")
@@ -193,17 +203,31 @@ def cpu_baseline(qkv_cpu, w, qg, kg, cos, sin, style, budget_s, dtype="bf16"):
 
 
 def _host():
-    """The host CPU model and the cores this process may use."""
-    model = "unknown"
+    """The host CPU as lscpu names it (model name, and vendor / family /
+    model / stepping, which identify the part when the name is generic),
+    and the cores this process may use."""
+    import subprocess
+    fields = {}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            key, _, val = line.partition(":")
+            fields[key.strip()] = val.strip()
+    except (OSError, subprocess.SubprocessError):
         pass
-    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0))}
+    model = fields.get("Model name")
+    if not model:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
+    ident = "/".join(fields.get(k, "?") for k in ("Vendor ID", "CPU family", "Model", "Stepping"))
+    return {"cpu_model": model or "unknown", "cpu_id": ident,
+            "nproc": len(os.sched_getaffinity(0))}
 
 
 def _single_core(sample_pass, reps=3):
@@ -306,7 +330,30 @@ def cpu_baseline_gn(x_cpu, w, g, b, param_dtype, dtype, nbytes, budget_s):
             **_host()}
 
 
-def time_launches(launch, stream, steps, warmup, flush_buf=None):
+class CacheFlush:
+    """Evicts the GPU caches (4 MB L2 per die, 256 MB Infinity Cache) between
+    timed calls with 1 GiB of traffic on the timed stream, outside the call's
+    event pair.  "clean" reads a 1 GiB buffer (a sum into one float): the
+    lines it leaves are clean, and the previous call's dirty lines are written
+    back while it runs.  "dirty" writes 1 GiB instead; its own dirty lines
+    are then written back during the next timed call and charged to it."""
+
+    def __init__(self, mode: str, device):
+        import torch
+        self.mode = mode
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device=device)
+        self.buf.fill_(1.0)
+        self.acc = torch.empty((), dtype=torch.float32, device=device)
+
+    def __call__(self, i: int):
+        import torch
+        if self.mode == "clean":
+            torch.sum(self.buf, dim=0, out=self.acc)
+        else:
+            self.buf.fill_(float(i))
+
+
+def time_launches(launch, stream, steps, warmup, flush=None):
     """Warm up, then time `steps` launches on `stream`.
 
     Without flushing, two passes of `steps` launches each:
@@ -314,8 +361,8 @@ def time_launches(launch, stream, steps, warmup, flush_buf=None):
        HIP event pair on `stream` (whole-job time: region ms and wall s);
     2. with a HIP event pair around every launch (per-launch µs).
     The per-launch events add a little host and queue work per launch, so
-    they stay out of the whole-job region.  With `flush_buf`, one pass: the
-    buffer is rewritten before every launch, outside its event pair.
+    they stay out of the whole-job region.  With `flush` (a CacheFlush), one
+    pass: the caches are flushed before every launch, outside its event pair.
 
     Returns (per-launch µs array, region ms, wall s)."""
     import numpy as np
@@ -326,7 +373,7 @@ def time_launches(launch, stream, steps, warmup, flush_buf=None):
     torch.cuda.synchronize()
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
-    if flush_buf is None:
+    if flush is None:
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         region0.record(stream)
@@ -342,15 +389,15 @@ def time_launches(launch, stream, steps, warmup, flush_buf=None):
     wall1 = time.perf_counter()
     region0.record(stream)
     for i in range(steps):
-        if flush_buf is not None:
+        if flush is not None:
             with torch.cuda.stream(stream):
-                flush_buf.fill_(float(i))
+                flush(i)
         starts[i].record(stream)
         launch()
         ends[i].record(stream)
     region1.record(stream)
     torch.cuda.synchronize()
-    if flush_buf is not None:
+    if flush is not None:
         wall = time.perf_counter() - wall1
         region_ms = region0.elapsed_time(region1)
     per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)]) * 1e3
@@ -375,7 +422,7 @@ def bench_fuse_scale_shift(args):
     nbytes = wl.adaln_bytes(w.rows, w.hidden, w.batches, mod_bytes=mod_bytes)
     stream = torch.cuda.Stream(device=dev)
     handle = stream.cuda_stream
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+    flush_buf = CacheFlush(args.flush_mode, dev) if args.flush else None
 
     def launch():
         qkr.fuse_scale_shift(x, scd, shd, out=y, eps=wl.EPS, rows_per_batch=w.rows_per_batch,
@@ -395,13 +442,16 @@ def bench_fuse_scale_shift(args):
         "config": {"workload": "%s: x %s [%d, %d], %d modulation row(s) %s%s%s"
                                % (w.key, dtype, w.rows, w.hidden, w.batches, args.mod_dtype,
                                   ", in place" if args.inplace else "",
-                                  ", cache flushed" if args.flush else ""),
+                                  (", cache flushed (%s)" % args.flush_mode) if args.flush
+                                  else ""),
                    "rows": w.rows, "hidden": w.hidden, "batches": w.batches, "data_dtype": dtype,
                    "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
                         "p10": round(float(np.percentile(per, 10)), 2),
                         "p90": round(float(np.percentile(per, 90)), 2)},
         "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
+        "pct_of_peak_median": round(100 * nbytes / (float(np.median(per)) * 1e-6) / 1e9
+                                    / PEAK_GBS, 2),
         "bytes_per_call": nbytes, "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
@@ -438,7 +488,7 @@ def bench_group_norm_silu(args):
     nbytes = wl.gn_bytes(w.n, w.channels, w.spatial, param_bytes=pbytes)
     stream = torch.cuda.Stream(device=dev)
     handle = stream.cuda_stream
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+    flush_buf = CacheFlush(args.flush_mode, dev) if args.flush else None
 
     def launch():
         qkr.group_norm_silu(x, gd, bd, w.groups, out=y, eps=wl.EPS, workspace=ws, stream=handle)
@@ -457,7 +507,8 @@ def bench_group_norm_silu(args):
         "config": {"workload": "%s: x %s [%d, %d, %d, %d], %d groups, %s affine%s%s"
                                % (w.key, dtype, w.n, w.channels, w.height, w.width, w.groups,
                                   args.mod_dtype, ", in place" if args.inplace else "",
-                                  ", cache flushed" if args.flush else ""),
+                                  (", cache flushed (%s)" % args.flush_mode) if args.flush
+                                  else ""),
                    "n": w.n, "channels": w.channels, "spatial": w.spatial, "groups": w.groups,
                    "schedule": sched, "chunk_elems": chunk, "workspace_bytes": need,
                    "data_dtype": dtype, "parallelism": "single GPU"},
@@ -465,6 +516,8 @@ def bench_group_norm_silu(args):
                         "p10": round(float(np.percentile(per, 10)), 2),
                         "p90": round(float(np.percentile(per, 90)), 2)},
         "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
+        "pct_of_peak_median": round(100 * nbytes / (float(np.median(per)) * 1e-6) / 1e9
+                                    / PEAK_GBS, 2),
         "bytes_per_call": nbytes, "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
@@ -592,6 +645,103 @@ def bench_eager_chain(args):
     return 0
 
 
+FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
+
+
+def bench_floor(args):
+    """The pass on the headline beside data-movement probes of its access
+    pattern (bench_floor.hip, a library of its own), in one process on one
+    stream, two rounds (the second in reverse order): the pass; the same Q/K
+    bytes read and written in place with the pass's mapping and cache policy
+    and no arithmetic; that plus the cos/sin rows staged in LDS; the Q/K
+    bytes with no V gaps; and a plain device copy of the Q/K bytes.  Prints
+    one JSON line; `value` is the pass's time over the full-pattern probe's."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_qk_amd as qkr
+    import workloads as wl
+    if not os.path.exists(FLOOR_LIB):
+        raise RuntimeError("bench_floor.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(FLOOR_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.qkr_floor_fused.argtypes = [vp, i64, i32, i64, vp, vp, i32, vp]
+    lib.qkr_floor_fused.restype = ctypes.c_int
+    w = wl.WORKLOADS[args.workload or "headline"]
+    style = args.style or w.styles[0]
+    T, H, D = w.tokens, w.heads, w.head_dim
+    if w.layout != "fused" or D != 128 or H > 40:
+        raise ValueError("the floor probe covers fused QKV with head_dim 128 and <= 40 heads")
+    dev = torch.device("cuda:0")
+    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16").to(dev)
+    flat = torch.empty((T, 2 * H * D), dtype=torch.bfloat16, device=dev)
+    flat.copy_(qkv[:, :2 * H * D])
+    src = flat.clone()
+    qg, kg = wl.norm_weights(w.seed, D)
+    cos, sin = wl.workload_tables(w, style)
+    g1, g2, c, s = qg.to(dev), kg.to(dev), cos.to(dev), sin.to(dev)
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+    qk_bytes = T * 2 * H * D * 2 * 2
+    table_bytes = T * D * 4 * 2
+
+    def probe(buf, stride, table):
+        def launch():
+            rc = lib.qkr_floor_fused(buf.data_ptr(), T, H, stride, c.data_ptr(), s.data_ptr(),
+                                     1 if table else 0, handle)
+            if rc != 0:
+                raise RuntimeError("qkr_floor_fused returned %d" % rc)
+        return launch
+
+    def copy():
+        with torch.cuda.stream(stream):
+            flat.copy_(src)
+
+    def the_pass():
+        qkr.qknorm_rope_fused(qkv, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS, style=style,
+                              stream=handle)
+
+    legs = [
+        ("pass", "the pass (qknorm_rope_fused), shared fp32 cos/sin", the_pass,
+         qk_bytes + table_bytes),
+        ("floor_table", "no arithmetic: Q/K in place with V gaps, cos/sin rows staged in LDS",
+         probe(qkv, 3 * H * D, True), qk_bytes + table_bytes),
+        ("floor_qk", "no arithmetic: Q/K in place with V gaps, no cos/sin",
+         probe(qkv, 3 * H * D, False), qk_bytes),
+        ("floor_flat", "no arithmetic: the Q/K bytes with no V gaps, no cos/sin",
+         probe(flat, 2 * H * D, False), qk_bytes),
+        ("copy", "device copy of the Q/K bytes (torch copy_, %d B each way)" % (qk_bytes // 2),
+         copy, qk_bytes),
+    ]
+    rounds = []
+    for order in (legs, legs[::-1]):
+        res = {}
+        for key, _, launch, nbytes in order:
+            per, region_ms, _ = time_launches(launch, stream, args.steps, args.warmup)
+            b2b = region_ms * 1e3 / args.steps
+            res[key] = {"back_to_back_us": round(b2b, 2), "mean_us": round(float(per.mean()), 2),
+                        "median_us": round(float(np.median(per)), 2),
+                        "pct_of_peak_back_to_back": round(100 * nbytes / (b2b * 1e-6) / 1e9
+                                                          / PEAK_GBS, 2)}
+        rounds.append(res)
+    b2b = {k: min(r[k]["back_to_back_us"] for r in rounds) for k, _, _, _ in legs}
+    result = {
+        "metric": "headline pass time over the data-movement floor of its access pattern",
+        "value": round(b2b["pass"] / b2b["floor_table"], 4), "unit": "x",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "%s: fused QKV bf16 [%d, 3x%dx%d], %s RoPE, shared fp32 cos/sin"
+                               % (w.key, T, H, D, style), "parallelism": "single GPU"},
+        "legs": {k: {"what": what, "bytes": nbytes} for k, what, _, nbytes in legs},
+        "rounds": rounds,
+        "best_back_to_back_us": b2b,
+    }
+    print(json.dumps(result))
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -615,6 +765,8 @@ def main():
         return bench_group_norm_silu(args)
     if args.op == "eager_chain":
         return bench_eager_chain(args)
+    if args.op == "floor":
+        return bench_floor(args)
     args.workload = args.workload or "headline"
     w = wl.WORKLOADS[args.workload]
     style = args.style or w.styles[0]
@@ -646,7 +798,7 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     handle = stream.cuda_stream
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+    flush_buf = CacheFlush(args.flush_mode, dev) if args.flush else None
 
     def launch():
         qkr.qknorm_rope_fused(**tensors, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS,
@@ -682,13 +834,16 @@ def main():
                                % (w.key, "fused QKV" if w.layout == "fused" else "separate q, k",
                                   dtype, T, "3x" if w.layout == "fused" else "", H, D, style,
                                   args.layout, args.cos_dtype,
-                                  ", cache flushed" if args.flush else ""),
+                                  (", cache flushed (%s)" % args.flush_mode) if args.flush
+                                  else ""),
                    "tokens": T, "heads": H, "head_dim": D, "layout": args.layout,
                    "style": style, "data_dtype": dtype, "parallelism": "single GPU"},
         "us_per_call": {"mean": round(mean_us, 2), "median": round(float(np.median(per)), 2),
                         "p10": round(float(np.percentile(per, 10)), 2),
                         "p90": round(float(np.percentile(per, 90)), 2)},
         "pct_of_peak": round(100 * achieved / PEAK_GBS, 2),
+        "pct_of_peak_median": round(100 * nbytes / (float(np.median(per)) * 1e-6) / 1e9
+                                    / PEAK_GBS, 2),
         "bytes_per_call": nbytes,
         "wall_s_timed": round(wall, 4),
         "kernel": info,

@@ -1,4 +1,5 @@
-"""Compile the HIP library ``libqknorm_rope.so`` for gfx950 with hipcc.
+"""Compile the HIP library ``libqknorm_rope.so`` for gfx950 with hipcc (and,
+beside it, bench.py's data-movement probe ``bench_floor.so``).
 
 Usage:  python -m diffusion_transformer_qk_amd.build [--save-temps DIR]
 """
@@ -16,6 +17,9 @@ SRCS = [os.path.join(PKG, "csrc", "qknorm_rope.hip"),
         os.path.join(PKG, "csrc", "group_norm_silu.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqknorm_rope.so")
+# bench.py's data-movement probe: its own library, outside libqknorm_rope.so
+FLOOR_SRC = os.path.join(ROOT, "bench_floor.hip")
+FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -62,12 +66,17 @@ def build(save_temps: str | None = None) -> str:
         objs.append(obj)
         procs.append((src, subprocess.Popen([hipcc(), *compile_flags, "-I", INCLUDE, "-c", src,
                                              "-o", obj])))
+    floor_tmp = FLOOR_LIB + ".tmp%d" % os.getpid()
+    procs.append((FLOOR_SRC, subprocess.Popen([hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I",
+                                               os.path.join(PKG, "csrc"), FLOOR_SRC, "-o",
+                                               floor_tmp])))
     failed = [src for src, proc in procs if proc.wait() != 0]
     if failed:
         raise RuntimeError("hipcc failed on " + ", ".join(failed))
     subprocess.run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp],
                    check=True)
     os.replace(tmp, LIB)
+    os.replace(floor_tmp, FLOOR_LIB)
     return LIB
 
 

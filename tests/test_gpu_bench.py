@@ -53,14 +53,31 @@ def test_step_reports(op):
     assert r["config"]["parallelism"] == "single GPU"
 
 
-def test_graph_and_flush_modes():
+@pytest.mark.parametrize("mode", ["clean", "dirty"])
+def test_graph_and_flush_modes(mode):
     """--graph adds the per-call time replayed from a captured HIP graph;
-    --flush rewrites 1 GiB before each call and reports the per-call rate."""
+    --flush evicts the caches before each call (by reading 1 GiB, or with
+    --flush-mode dirty by writing it) and reports the per-call rate."""
     g = run_bench("--workload", "tiny", "--graph", "--steps", "20", "--warmup", "2",
                   "--no-cpu-baseline")
     assert g["graph_us_per_call"] > 0
-    f = run_bench("--workload", "mid", "--flush", "--steps", "5", "--warmup", "1",
-                  "--no-cpu-baseline")
-    assert "cache flushed" in f["config"]["workload"]
+    f = run_bench("--workload", "mid", "--flush", "--flush-mode", mode, "--steps", "5",
+                  "--warmup", "1", "--no-cpu-baseline")
+    assert "cache flushed (%s)" % mode in f["config"]["workload"]
     assert abs(f["value"] - f["roofline"]["achieved"]) <= 0.1
+    assert f["pct_of_peak_median"] > 0
+
+
+def test_floor_report():
+    """--op floor times the pass beside its no-arithmetic access-pattern
+    probes (a library of their own) in two rounds; the pass cannot beat the
+    probe that moves the same bytes the same way."""
+    r = run_bench("--op", "floor", "--steps", "10", "--warmup", "2")
+    legs = set(r["legs"])
+    assert legs == {"pass", "floor_table", "floor_qk", "floor_flat", "copy"}
+    assert len(r["rounds"]) == 2 and all(set(x) == legs for x in r["rounds"])
+    b = r["best_back_to_back_us"]
+    assert all(v > 0 for v in b.values())
+    assert r["value"] == round(b["pass"] / b["floor_table"], 4)
+    assert r["value"] > 0.9
 
