@@ -802,11 +802,13 @@ extern "C" int32_t dit_group_norm_silu_schedule(int64_t n, int32_t channels, int
 namespace {
 
 // The call, with the lagged schedule's polls per unpublished word.
-int run_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int64_t spatial,
-                        int32_t groups, const void* gamma, const void* beta, int32_t param_dtype,
-                        float eps, int32_t dtype, void* workspace, int64_t workspace_bytes,
-                        void* stream, int32_t wait_polls)
+// Every check of a call's arguments but the workspace's (no HIP call).  On
+// QKR_OK, *need holds the workspace bytes the call takes (0 for n == 0).
+int check_call(const void* x, const void* y, int64_t n, int32_t channels, int64_t spatial,
+               int32_t groups, const void* gamma, const void* beta, int32_t param_dtype,
+               float eps, int32_t dtype, int64_t* need)
 {
+    *need = 0;
     if (dtype < QKR_BF16 || dtype > QKR_FP32 || param_dtype < QKR_BF16 || param_dtype > QKR_FP32)
         return QKR_ERR_ARG;
     if (dtype == QKR_FP32)
@@ -831,7 +833,26 @@ int run_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int
     if ((x != y && overlaps(x, bytes, y, bytes)) || overlaps(y, bytes, gamma, param_bytes) ||
         overlaps(y, bytes, beta, param_bytes))
         return QKR_ERR_ARG;
-    const int64_t need = chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
+    *need = chunks > 1 ? pairs * chunks * 2 * (int64_t)sizeof(float) : 0;
+    return QKR_OK;
+}
+
+int run_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int64_t spatial,
+                        int32_t groups, const void* gamma, const void* beta, int32_t param_dtype,
+                        float eps, int32_t dtype, void* workspace, int64_t workspace_bytes,
+                        void* stream, int32_t wait_polls)
+{
+    int64_t need = 0;
+    const int rc = check_call(x, y, n, channels, spatial, groups, gamma, beta, param_dtype, eps,
+                              dtype, &need);
+    if (rc != QKR_OK || n == 0)
+        return rc;
+    int64_t chunks = 0, pairs = 0;
+    int vpt = 0;
+    check_shape(n, channels, spatial, groups, &chunks, &pairs, &vpt);
+    const int64_t gsize = (int64_t)(channels / groups) * spatial;
+    const uint64_t bytes = (uint64_t)(pairs * gsize) * 2u;
+    const uint64_t param_bytes = (uint64_t)channels * (param_dtype == QKR_FP32 ? 4u : 2u);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return QKR_ERR_WORKSPACE;
     // the workspace is written too: apart from every other buffer
