@@ -7,7 +7,8 @@ The passes run in hand-written HIP kernels behind the C ABI of
 (``libqknorm_rope.so``); this package is the thin Python binding over it.
 """
 from .binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, QkrError, dit_fuse_scale_shift_raw, dit_group_norm_silu_raw,
+    EXPORTS, LIB_PATH, QkrError, dit_fuse_scale_shift_raw, dit_group_norm_silu_noalloc_raw,
+    dit_group_norm_silu_raw,
     fuse_scale_shift, group_norm_silu, group_norm_silu_schedule,
     group_norm_silu_workspace_size, kernel_info,
     load_library, qknorm_rope_fused, qknorm_rope_fused_raw, strerror, version,
@@ -16,5 +17,6 @@ from .binding import (  # noqa: F401
 __all__ = ["qknorm_rope_fused", "qknorm_rope_fused_raw", "fuse_scale_shift",
            "dit_fuse_scale_shift_raw", "group_norm_silu", "group_norm_silu_schedule",
            "group_norm_silu_workspace_size",
-           "dit_group_norm_silu_raw", "kernel_info", "load_library", "strerror", "version",
+           "dit_group_norm_silu_raw", "dit_group_norm_silu_noalloc_raw", "kernel_info",
+           "load_library", "strerror", "version",
            "QkrError", "EXPORTS", "LIB_PATH"]

@@ -21,6 +21,8 @@ QKR_OK = 0
 QKR_ERR_NULL, QKR_ERR_SHAPE, QKR_ERR_ALIGN = -1, -2, -3
 QKR_ERR_UNSUPPORTED, QKR_ERR_MODE, QKR_ERR_HIP, QKR_ERR_ARG = -4, -5, -6, -7
 QKR_ERR_WORKSPACE = -8
+QKR_ERR_SCRATCH = -9
+GN_NOALLOC_WORKSPACE_MAX = 1 << 20
 QKR_BF16, QKR_FP16, QKR_FP32 = 0, 1, 2
 QKR_COS_SHARED, QKR_COS_PER_HEAD = 0, 1
 QKR_ROPE_INTERLEAVED, QKR_ROPE_ROTATE_HALF = 0, 1
@@ -32,7 +34,7 @@ TENSORS = {"fused": QKR_TENSORS_FUSED, "pair": QKR_TENSORS_PAIR, "one": QKR_TENS
 EXPORTS = ("qknorm_rope_fused", "qknorm_rope_strerror", "qknorm_rope_version",
            "qknorm_rope_kernel_info", "dit_fuse_scale_shift",
            "dit_group_norm_silu_workspace_size", "dit_group_norm_silu_schedule",
-           "dit_group_norm_silu")
+           "dit_group_norm_silu", "dit_group_norm_silu_noalloc")
 MOD_DTYPES = {"bf16": QKR_BF16, "fp16": QKR_FP16, "fp32": QKR_FP32}
 
 
@@ -84,6 +86,9 @@ def load_library(path: str = LIB_PATH):
     lib.dit_group_norm_silu.argtypes = [vp, vp, i64, i32, i64, i32, vp, vp, i32, f32, i32, vp, i64,
                                         vp]
     lib.dit_group_norm_silu.restype = ctypes.c_int
+    lib.dit_group_norm_silu_noalloc.argtypes = [vp, vp, i64, i32, i64, i32, vp, vp, i32, f32,
+                                                i32, vp]
+    lib.dit_group_norm_silu_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -348,6 +353,18 @@ def dit_group_norm_silu_raw(x: int, y: int, n: int, channels: int, spatial: int,
     return int(lib.dit_group_norm_silu(x or None, y or None, n, channels, spatial, groups,
                                        gamma or None, beta or None, param_dtype, eps, dtype,
                                        workspace or None, workspace_bytes, stream or None))
+
+
+def dit_group_norm_silu_noalloc_raw(x: int, y: int, n: int, channels: int, spatial: int,
+                                    groups: int, gamma: int, beta: int, param_dtype: int,
+                                    eps: float, dtype: int, stream: int) -> int:
+    """The group-norm entry point that allocates nothing (its workspace is the
+    library's fixed per-GPU scratch), with integer pointers; returns the raw
+    status."""
+    lib = load_library()
+    return int(lib.dit_group_norm_silu_noalloc(x or None, y or None, n, channels, spatial, groups,
+                                               gamma or None, beta or None, param_dtype, eps,
+                                               dtype, stream or None))
 
 
 def group_norm_silu(x, gamma, beta, groups: int, *, out=None, eps: float = 1e-6,

@@ -33,6 +33,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "host_common.h"
 #include "group_norm_silu.h"
@@ -903,6 +905,63 @@ int run_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------- fixed scratch
+//
+// The workspace of dit_group_norm_silu_noalloc: one copy of this array per
+// GPU, held until the process ends.  Host code never passes `scratch` itself
+// (in host code the name is a host-side stand-in, not a device address): it
+// passes the device address hipGetSymbolAddress gives for the current device,
+// looked up once per device.
+static __device__ __align__(256) uint8_t scratch[QKR_GN_NOALLOC_WORKSPACE_MAX];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_status[kMaxDevices];
+
+// The device address of `scratch` on the current device.
+int scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QKR_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = ptr;
+    });
+    if (g_scratch_status[dev] != hipSuccess || !g_scratch_ptr[dev])
+        return QKR_ERR_HIP;
+    *out = g_scratch_ptr[dev];
+    return QKR_OK;
+}
+
+}  // namespace
+
+extern "C" int dit_group_norm_silu_noalloc(const void* x, void* y, int64_t n, int32_t channels,
+                                           int64_t spatial, int32_t groups, const void* gamma,
+                                           const void* beta, int32_t param_dtype, float eps,
+                                           int32_t dtype, void* stream)
+{
+    int64_t need = 0;
+    const int rc = check_call(x, y, n, channels, spatial, groups, gamma, beta, param_dtype, eps,
+                              dtype, &need);
+    if (rc != QKR_OK || n == 0)
+        return rc;
+    if (need > QKR_GN_NOALLOC_WORKSPACE_MAX)
+        return QKR_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        const int r = scratch_address(&ws);
+        if (r != QKR_OK)
+            return r;
+    }
+    return run_group_norm_silu(x, y, n, channels, spatial, groups, gamma, beta, param_dtype, eps,
+                               dtype, ws, need, stream, kWaitPolls);
+}
 
 extern "C" int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels,
                                    int64_t spatial, int32_t groups, const void* gamma,

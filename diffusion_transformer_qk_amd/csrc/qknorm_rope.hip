@@ -675,6 +675,8 @@ extern "C" const char* qknorm_rope_strerror(int status)
     case QKR_ERR_HIP: return "HIP launch or query failed";
     case QKR_ERR_ARG: return "eps not finite and > 0, an enum out of range, or a written buffer overlapping another";
     case QKR_ERR_WORKSPACE: return "workspace missing or smaller than required";
+    case QKR_ERR_SCRATCH: return "the call needs more workspace than the library's fixed scratch "
+                                 "(QKR_GN_NOALLOC_WORKSPACE_MAX); pass a workspace instead";
     default: return "unknown status";
     }
 }

@@ -103,6 +103,40 @@ int dit_group_norm_silu(const void* x, void* y, int64_t n, int32_t channels, int
                         float eps, int32_t dtype, void* workspace, int64_t workspace_bytes,
                         void* stream);
 
+/* Largest workspace dit_group_norm_silu_noalloc can use (1 MiB per GPU). */
+#define QKR_GN_NOALLOC_WORKSPACE_MAX ((int64_t)1 << 20)
+
+/*
+ * dit_group_norm_silu_noalloc -- dit_group_norm_silu for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, kernels and output
+ * bits, with the workspace taken from a fixed array inside the library
+ * instead of a caller's buffer.
+ *
+ * The array is QKR_GN_NOALLOC_WORKSPACE_MAX bytes, one copy per GPU the
+ * library runs on, held until the process ends; its device address is
+ * looked up once per device, on the first call that needs it.  The call
+ * allocates and frees nothing.  A call whose workspace size
+ * (dit_group_norm_silu_workspace_size) exceeds the maximum returns
+ * QKR_ERR_SCRATCH with nothing enqueued (for example more than 131,072
+ * chunks of 16,384 elements; groups of one chunk need no workspace at all).
+ *
+ * Every call on one GPU shares that GPU's array, and each call starts by
+ * initialising what it reads (the lagged schedule marks its words
+ * unpublished; the two-pass schedule writes every partial before reading
+ * it).  Calls that overlap in time on one GPU -- on different streams, or
+ * from different threads without ordering -- race on the array and must not
+ * be issued.
+ *
+ * Arguments, checks and the other status codes are those of
+ * dit_group_norm_silu without workspace and workspace_bytes.  QKR_ERR_HIP
+ * is also returned when the array's address cannot be looked up.
+ */
+int dit_group_norm_silu_noalloc(const void* x, void* y, int64_t n, int32_t channels,
+                                int64_t spatial, int32_t groups, const void* gamma,
+                                const void* beta, int32_t param_dtype, float eps, int32_t dtype,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

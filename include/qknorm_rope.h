@@ -50,7 +50,8 @@ enum {
     QKR_ERR_HIP = -6,         /* the kernel launch (or an attribute query) failed     */
     QKR_ERR_ARG = -7,         /* eps not finite and > 0, an enum out of range, or a   */
                               /* buffer the call writes overlapping another buffer    */
-    QKR_ERR_WORKSPACE = -8    /* workspace missing or smaller than required           */
+    QKR_ERR_WORKSPACE = -8,   /* workspace missing or smaller than required           */
+    QKR_ERR_SCRATCH = -9      /* the call needs more than the library's fixed scratch  */
 };
 
 /* Element types. */

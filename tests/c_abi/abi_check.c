@@ -85,6 +85,12 @@ int main(void)
                                NULL), QKR_ERR_UNSUPPORTED);
     EXPECT(dit_group_norm_silu(a, b, 0, 512, 64, 32, a, a, QKR_FP32, 1e-6f, QKR_BF16, NULL, 0,
                                NULL), QKR_OK);
+    /* the entry point without workspace: a call beyond its fixed scratch is
+     * refused before any HIP call; n == 0 is a no-op */
+    EXPECT(dit_group_norm_silu_noalloc(a, (void*)(uintptr_t)0x1000000000ull, 65, 512, 65536, 32, a,
+                                       a, QKR_FP32, 1e-6f, QKR_BF16, NULL), QKR_ERR_SCRATCH);
+    EXPECT(dit_group_norm_silu_noalloc(a, b, 0, 64, 64, 8, a, a, QKR_FP32, 1e-6f, QKR_BF16, NULL),
+           QKR_OK);
     printf("ok\n");
     return 0;
 }

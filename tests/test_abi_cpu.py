@@ -339,3 +339,37 @@ def test_library_reads_no_environment():
                          text=True, check=True).stdout
     names = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
     assert not names & {"getenv", "secure_getenv", "__secure_getenv"}, names & {"getenv"}
+
+
+def gn_noalloc(**over):
+    args = dict(x=A, y=A + (1 << 36), n=1, channels=64, spatial=64, groups=8, gamma=A, beta=A,
+                param_dtype=b.QKR_FP32, eps=1e-6, dtype=b.QKR_BF16, stream=0)
+    args.update(over)
+    return qkr.dit_group_norm_silu_noalloc_raw(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n=65, channels=512, spatial=65536, groups=32), b.QKR_ERR_SCRATCH),
+    (dict(dtype=b.QKR_FP32), b.QKR_ERR_UNSUPPORTED),
+    (dict(param_dtype=7), b.QKR_ERR_ARG),
+    (dict(eps=0.0), b.QKR_ERR_ARG),
+    (dict(channels=63), b.QKR_ERR_SHAPE),
+    (dict(spatial=12), b.QKR_ERR_UNSUPPORTED),
+    (dict(x=0), b.QKR_ERR_NULL),
+    (dict(y=MIS), b.QKR_ERR_ALIGN),
+    (dict(n=0), b.QKR_OK),
+])
+def test_group_norm_noalloc_checks_before_any_hip_call(over, code):
+    """The entry point without workspace rejects, before any HIP call, what
+    dit_group_norm_silu rejects, and a call whose workspace would exceed the
+    fixed scratch (65 x 32 groups of 64 chunks: 1 MiB + 64 KiB)."""
+    assert gn_noalloc(**over) == code
+
+
+def test_group_norm_noalloc_scratch_limit():
+    """The largest workspace the fixed scratch takes is 1 MiB: 131,072 chunk
+    words of 8 bytes, one more chunk is refused."""
+    assert b.GN_NOALLOC_WORKSPACE_MAX == 1 << 20
+    assert qkr.group_norm_silu_workspace_size(64, 512, 65536, 32) == 1 << 20
+    assert qkr.group_norm_silu_workspace_size(65, 512, 65536, 32) > 1 << 20
+    assert "scratch" in qkr.strerror(b.QKR_ERR_SCRATCH)
