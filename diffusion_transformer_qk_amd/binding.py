@@ -65,6 +65,13 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(
             "libqknorm_rope.so is not built (%s); run __graft_entry__.build() or "
             "python -m diffusion_transformer_qk_amd.build" % path)
+    # torch first: it carries its own HIP runtime, and the library's HIP
+    # dependency must resolve to that one.  Loaded the other way round, the
+    # process holds two runtimes and the library's sees no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
     lib.qknorm_rope_fused.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, f32, vp, vp,
