@@ -91,9 +91,10 @@ def recorded_traffic(path: str, op: str, key: str):
     return None if entry is None else entry.get("bytes_per_launch")
 
 
-def measured_traffic(workload: str, layout: str, style: str):
+def measured_traffic(workload: str, layout: str, style: str, dtype: str):
     """HBM bytes per launch of the QK-norm + RoPE kernel, if still current."""
-    return recorded_traffic(TRAFFIC_FILE, "qknorm_rope", "%s/%s/%s" % (workload, layout, style))
+    return recorded_traffic(TRAFFIC_FILE, "qknorm_rope",
+                            "%s/%s/%s/%s" % (workload, layout, style, dtype))
 
 
 def parse():
@@ -649,13 +650,17 @@ FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
 
 
 def bench_floor(args):
-    """The pass on the headline beside data-movement probes of its access
-    pattern (bench_floor.hip, a library of its own), in one process on one
-    stream, two rounds (the second in reverse order): the pass; the same Q/K
-    bytes read and written in place with the pass's mapping and cache policy
-    and no arithmetic; that plus the cos/sin rows staged in LDS; the Q/K
-    bytes with no V gaps; and a plain device copy of the Q/K bytes.  Prints
-    one JSON line; `value` is the pass's time over the full-pattern probe's."""
+    """The pass beside data-movement probes of its access pattern
+    (bench_floor.hip, a library of its own) on one workload, in one process
+    on one stream, two rounds (the second in reverse order).  Legs: the pass;
+    the probe that moves the same bytes the same way with no arithmetic
+    (floor_table, with the cos/sin staging); the Q/K bytes in place with the
+    same barrier (floor_phase) and with none (floor_qk); the Q/K bytes read
+    only and written only; for a fused buffer the Q/K bytes with no V gaps;
+    and a plain device copy of the Q/K bytes.  Back-to-back time per call,
+    or with --flush the mean per-call time with the caches evicted before
+    each call.  Prints one JSON line; `value` is the pass's time over
+    floor_table's."""
     import ctypes
 
     import numpy as np
@@ -666,33 +671,49 @@ def bench_floor(args):
     if not os.path.exists(FLOOR_LIB):
         raise RuntimeError("bench_floor.so is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(FLOOR_LIB)
-    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    lib.qkr_floor_fused.argtypes = [vp, i64, i32, i64, vp, vp, i32, vp]
-    lib.qkr_floor_fused.restype = ctypes.c_int
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    lib.qkr_floor.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp, u32, i32, vp]
+    lib.qkr_floor.restype = ctypes.c_int
     w = wl.WORKLOADS[args.workload or "headline"]
     style = args.style or w.styles[0]
+    dtype = args.dtype or w.dtypes[0]
     T, H, D = w.tokens, w.heads, w.head_dim
-    if w.layout != "fused" or D != 128 or H > 40:
-        raise ValueError("the floor probe covers fused QKV with head_dim 128 and <= 40 heads")
+    if D != 128 or H > 48:
+        raise ValueError("the floor probes cover head_dim 128 with at most 48 heads")
     dev = torch.device("cuda:0")
-    qkv = wl.fused_qkv(w.seed, T, H, D, "bf16").to(dev)
-    flat = torch.empty((T, 2 * H * D), dtype=torch.bfloat16, device=dev)
-    flat.copy_(qkv[:, :2 * H * D])
-    src = flat.clone()
     qg, kg = wl.norm_weights(w.seed, D)
     cos, sin = wl.workload_tables(w, style)
     g1, g2, c, s = qg.to(dev), kg.to(dev), cos.to(dev), sin.to(dev)
+    fused = w.layout == "fused"
+    if fused:
+        qkv = wl.fused_qkv(w.seed, T, H, D, dtype).to(dev)
+        probe_buf = qkv.clone()
+        tensors = dict(qkv=qkv)
+        x0, x1, stride = probe_buf.data_ptr(), probe_buf.data_ptr() + H * D * 2, 3 * H * D
+        flat = torch.empty((T, 2 * H * D), dtype=qkv.dtype, device=dev)
+        flat.copy_(qkv[:, :2 * H * D])
+    else:
+        q_cpu, k_cpu = wl.separate_qk(w.seed, T, H, D, (dtype,))[dtype]
+        tensors = dict(q=q_cpu.to(dev), k=k_cpu.to(dev))
+        pq, pk = tensors["q"].clone(), tensors["k"].clone()
+        x0, x1, stride = pq.data_ptr(), pk.data_ptr(), H * D
+        flat = torch.cat([tensors["q"].view(T, -1), tensors["k"].view(T, -1)], dim=1)
+    src = flat.clone()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
     stream = torch.cuda.Stream(device=dev)
     handle = stream.cuda_stream
     qk_bytes = T * 2 * H * D * 2 * 2
     table_bytes = T * D * 4 * 2
+    magic = 0x9E3779B9
 
-    def probe(buf, stride, table):
+    def probe(mode, a0=None, a1=None, row=None):
+        b0, b1, st = (x0, x1, stride) if a0 is None else (a0, a1, row)
+
         def launch():
-            rc = lib.qkr_floor_fused(buf.data_ptr(), T, H, stride, c.data_ptr(), s.data_ptr(),
-                                     1 if table else 0, handle)
+            rc = lib.qkr_floor(b0, b1, T, H, st, c.data_ptr(), s.data_ptr(), sink.data_ptr(),
+                               magic, mode, handle)
             if rc != 0:
-                raise RuntimeError("qkr_floor_fused returned %d" % rc)
+                raise RuntimeError("qkr_floor returned %d" % rc)
         return launch
 
     def copy():
@@ -700,43 +721,54 @@ def bench_floor(args):
             flat.copy_(src)
 
     def the_pass():
-        qkr.qknorm_rope_fused(qkv, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS, style=style,
-                              stream=handle)
+        qkr.qknorm_rope_fused(**tensors, q_gamma=g1, k_gamma=g2, cos=c, sin=s, eps=wl.EPS,
+                              style=style, stream=handle)
 
     legs = [
         ("pass", "the pass (qknorm_rope_fused), shared fp32 cos/sin", the_pass,
          qk_bytes + table_bytes),
-        ("floor_table", "no arithmetic: Q/K in place with V gaps, cos/sin rows staged in LDS",
-         probe(qkv, 3 * H * D, True), qk_bytes + table_bytes),
-        ("floor_qk", "no arithmetic: Q/K in place with V gaps, no cos/sin",
-         probe(qkv, 3 * H * D, False), qk_bytes),
-        ("floor_flat", "no arithmetic: the Q/K bytes with no V gaps, no cos/sin",
-         probe(flat, 2 * H * D, False), qk_bytes),
-        ("copy", "device copy of the Q/K bytes (torch copy_, %d B each way)" % (qk_bytes // 2),
-         copy, qk_bytes),
+        ("floor_table", "no arithmetic: Q/K in place, cos/sin rows staged in LDS behind a barrier",
+         probe(1), qk_bytes + table_bytes),
+        ("floor_phase", "no arithmetic: Q/K in place, a barrier between loads and stores",
+         probe(2), qk_bytes),
+        ("floor_qk", "no arithmetic: Q/K in place, no barrier", probe(0), qk_bytes),
+        ("read_only", "the Q/K loads alone", probe(3), qk_bytes // 2),
+        ("write_only", "the Q/K stores alone (zeros)", probe(4), qk_bytes // 2),
     ]
+    if fused:
+        legs.append(("floor_flat", "no arithmetic: the Q/K bytes with no V gaps, no barrier",
+                     probe(0, flat.data_ptr(), flat.data_ptr() + H * D * 2, 2 * H * D),
+                     qk_bytes))
+    legs.append(("copy", "device copy of the Q/K bytes (torch copy_, %d B each way)"
+                 % (qk_bytes // 2), copy, qk_bytes))
+    flush = CacheFlush(args.flush_mode, dev) if args.flush else None
     rounds = []
     for order in (legs, legs[::-1]):
         res = {}
         for key, _, launch, nbytes in order:
-            per, region_ms, _ = time_launches(launch, stream, args.steps, args.warmup)
-            b2b = region_ms * 1e3 / args.steps
-            res[key] = {"back_to_back_us": round(b2b, 2), "mean_us": round(float(per.mean()), 2),
+            per, region_ms, _ = time_launches(launch, stream, args.steps, args.warmup, flush)
+            us = float(per.mean()) if flush else region_ms * 1e3 / args.steps
+            res[key] = {"us": round(us, 2), "mean_us": round(float(per.mean()), 2),
                         "median_us": round(float(np.median(per)), 2),
-                        "pct_of_peak_back_to_back": round(100 * nbytes / (b2b * 1e-6) / 1e9
-                                                          / PEAK_GBS, 2)}
+                        "pct_of_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2)}
         rounds.append(res)
-    b2b = {k: min(r[k]["back_to_back_us"] for r in rounds) for k, _, _, _ in legs}
+    best = {k: min(r[k]["us"] for r in rounds) for k, _, _, _ in legs}
     result = {
-        "metric": "headline pass time over the data-movement floor of its access pattern",
-        "value": round(b2b["pass"] / b2b["floor_table"], 4), "unit": "x",
+        "metric": "pass time over the data-movement floor of its access pattern",
+        "value": round(best["pass"] / best["floor_table"], 4), "unit": "x",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "%s: fused QKV bf16 [%d, 3x%dx%d], %s RoPE, shared fp32 cos/sin"
-                               % (w.key, T, H, D, style), "parallelism": "single GPU"},
+        "config": {"workload": "%s: %s %s [%d, %s%dx%d], %s RoPE, shared fp32 cos/sin%s"
+                               % (w.key, "fused QKV" if fused else "separate q, k", dtype, T,
+                                  "3x" if fused else "", H, D, style,
+                                  (", cache flushed (%s)" % args.flush_mode) if args.flush
+                                  else ""),
+                   "timing": "mean per call, caches flushed before each" if args.flush
+                             else "back to back", "parallelism": "single GPU"},
         "legs": {k: {"what": what, "bytes": nbytes} for k, what, _, nbytes in legs},
         "rounds": rounds,
-        "best_back_to_back_us": b2b,
+        "best_us": best,
+        "read_then_write_us": round(best["read_only"] + best["write_only"], 2),
     }
     print(json.dumps(result))
     return 0
@@ -816,7 +848,8 @@ def main():
                            qkr.binding.QKR_FP16 if dtype == "fp16" else qkr.binding.QKR_BF16,
                            heads=H, tokens=T, tensors="fused" if w.layout == "fused" else "pair")
 
-    traffic = measured_traffic(args.workload, args.layout, style)
+    traffic = (measured_traffic(args.workload, args.layout, style, dtype)
+               if args.cos_dtype == "fp32" else None)
     result = {
         "metric": METRIC,
         "value": round(value, 1),

@@ -319,6 +319,15 @@ __device__ __forceinline__ void load_chunk(const Params& p, const uint16_t* row,
 
 // ---------------------------------------------------------------- the kernel
 //
+// Waves per SIMD the register allocation must allow: 8 (64 VGPRs) for the
+// shared-row kernels with at most 6 head iterations in flight, so that a
+// grid of up to 2,048 workgroups (4,096 fused tokens) is resident at once
+// instead of leaving a second, mostly idle round (measured: the mid-size
+// 4096 x 3*24*128 call 19.0 -> 18.1 us back to back, the 5-head shard
+// 42.6 -> 39.8 us; no spills).  Otherwise the register count the code needs.
+template <bool PER_HEAD, int U>
+constexpr int min_waves_per_simd() { return (!PER_HEAD && U <= 6) ? 8 : 1; }
+
 // U      head iterations (of 64/L heads per wave) whose loads are in flight
 //        before any arithmetic;
 // WAVES  waves per workgroup (WAVES/2 tokens of Q and K per workgroup);
@@ -327,7 +336,8 @@ __device__ __forceinline__ void load_chunk(const Params& p, const uint16_t* row,
 
 template <int D, int STYLE, bool PER_HEAD, bool COS_BF16, bool X_FP16, int U, int WAVES, int NT,
           int ORDER>
-__global__ __launch_bounds__(WAVES * kWave) void qknorm_rope_kernel(const Params p)
+__global__ __launch_bounds__(WAVES * kWave, (min_waves_per_simd<PER_HEAD, U>()))
+void qknorm_rope_kernel(const Params p)
 {
     constexpr int L = D / kVec;        // lanes per head
     constexpr int HPI = kWave / L;     // heads per wave iteration

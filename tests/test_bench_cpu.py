@@ -20,17 +20,18 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_traffic_is_reported_only_for_the_measured_source(tmp_path, monkeypatch):
     rec = {"kernel_source_sha256_16": bench.kernel_source_hash(),
-           "runs": {"headline/shared/interleaved": {"bytes_per_launch": 123}}}
+           "runs": {"headline/shared/interleaved/bf16": {"bytes_per_launch": 123}}}
     path = os.path.join(tmp_path, "t.json")
     with open(path, "w") as f:
         json.dump(rec, f)
     monkeypatch.setattr(bench, "TRAFFIC_FILE", path)
-    assert bench.measured_traffic("headline", "shared", "interleaved") == 123
-    assert bench.measured_traffic("headline", "per_head", "interleaved") is None
+    assert bench.measured_traffic("headline", "shared", "interleaved", "bf16") == 123
+    assert bench.measured_traffic("headline", "per_head", "interleaved", "bf16") is None
+    assert bench.measured_traffic("headline", "shared", "interleaved", "fp16") is None
     rec["kernel_source_sha256_16"] = "0" * 16
     with open(path, "w") as f:
         json.dump(rec, f)
-    assert bench.measured_traffic("headline", "shared", "interleaved") is None
+    assert bench.measured_traffic("headline", "shared", "interleaved", "bf16") is None
 
 
 @pytest.mark.parametrize("op,key", [("fuse_scale_shift", "adaln_wan/bf16/fp32/out"),

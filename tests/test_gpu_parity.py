@@ -117,6 +117,15 @@ def assert_v_untouched(out, inp, H, D):
     assert torch.equal(a, b), "V slice changed"
 
 
+def figures(pairs, dtype):
+    """(largest |o|, fraction of elements that differ from the oracle's
+    round-to-nearest-even image) over (got, ref) pairs."""
+    o = max(float(np.abs(r).max()) for _, r in pairs)
+    diff = sum(int(np.count_nonzero(g.reshape(r.shape) != oracle.round_to(r, dtype)))
+               for g, r in pairs)
+    return o, diff / sum(r.size for _, r in pairs)
+
+
 def compare_fused(out, qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout="shared",
                   what=""):
     T = qkv_cpu.shape[0]
@@ -125,6 +134,8 @@ def compare_fused(out, qkv_cpu, x_dtype, H, D, qg, kg, cos, sin, style, layout="
     m1 = check_close(got[:, 0], q_ref, x_dtype, what + " Q")
     m2 = check_close(got[:, 1], k_ref, x_dtype, what + " K")
     assert_v_untouched(out, qkv_cpu, H, D)
+    o, frac = figures([(got[:, 0], q_ref), (got[:, 1], k_ref)], x_dtype)
+    print("%s: max_abs %.4g max|o| %.3g RNE-disagreement %.2e" % (what, max(m1, m2), o, frac))
     return max(m1, m2)
 
 
@@ -216,6 +227,9 @@ def test_flux_workload_separate_q_k(x_dtype):
     k_ref = oracle.qknorm_rope(wl.u16(k), x_dtype, gamma=kg.numpy(), **kw)
     mq = check_close(_decode(qd, x_dtype), q_ref, x_dtype, "flux q")
     mk = check_close(_decode(kd, x_dtype), k_ref, x_dtype, "flux k")
+    o, frac = figures([(_decode(qd, x_dtype), q_ref), (_decode(kd, x_dtype), k_ref)], x_dtype)
+    print("flux %s: max_abs %.4g max|o| %.3g RNE-disagreement %.2e" % (x_dtype, max(mq, mk), o,
+                                                                     frac))
     # text tokens sit at position 0: their output is the norm alone
     print("flux", x_dtype, "max_abs", mq, mk)
 
