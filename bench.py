@@ -655,9 +655,13 @@ def bench_floor(args):
     on one stream, two rounds (the second in reverse order).  Legs: the pass;
     the probe that moves the same bytes the same way with no arithmetic
     (floor_table, with the cos/sin staging); the Q/K bytes in place with the
-    same barrier (floor_phase) and with none (floor_qk); the Q/K bytes read
-    only and written only; for a fused buffer the Q/K bytes with no V gaps;
-    and a plain device copy of the Q/K bytes.  Back-to-back time per call,
+    same phases (every wave's loads complete, then a workgroup barrier, then
+    the stores: floor_phase), with the wave's wait but no barrier
+    (floor_wave, and floor_wave_uncapped without the pass's residency cap),
+    and with each store issued as its load arrives (floor_qk); the Q/K bytes
+    read only and written only; for a fused buffer the Q/K bytes with no V
+    gaps; and a plain device copy of the Q/K bytes.  Every probe but
+    floor_wave_uncapped applies the pass's residency rule.  Back-to-back time per call,
     or with --flush the mean per-call time with the caches evicted before
     each call.  Prints one JSON line; `value` is the pass's time over
     floor_table's."""
@@ -672,7 +676,7 @@ def bench_floor(args):
         raise RuntimeError("bench_floor.so is not built; run __graft_entry__.build()")
     lib = ctypes.CDLL(FLOOR_LIB)
     vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
-    lib.qkr_floor.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp, u32, i32, vp]
+    lib.qkr_floor.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp, u32, i32, i32, vp]
     lib.qkr_floor.restype = ctypes.c_int
     w = wl.WORKLOADS[args.workload or "headline"]
     style = args.style or w.styles[0]
@@ -706,12 +710,12 @@ def bench_floor(args):
     table_bytes = T * D * 4 * 2
     magic = 0x9E3779B9
 
-    def probe(mode, a0=None, a1=None, row=None):
+    def probe(mode, a0=None, a1=None, row=None, cap=1):
         b0, b1, st = (x0, x1, stride) if a0 is None else (a0, a1, row)
 
         def launch():
             rc = lib.qkr_floor(b0, b1, T, H, st, c.data_ptr(), s.data_ptr(), sink.data_ptr(),
-                               magic, mode, handle)
+                               magic, mode, cap, handle)
             if rc != 0:
                 raise RuntimeError("qkr_floor returned %d" % rc)
         return launch
@@ -729,9 +733,14 @@ def bench_floor(args):
          qk_bytes + table_bytes),
         ("floor_table", "no arithmetic: Q/K in place, cos/sin rows staged in LDS behind a barrier",
          probe(1), qk_bytes + table_bytes),
-        ("floor_phase", "no arithmetic: Q/K in place, a barrier between loads and stores",
-         probe(2), qk_bytes),
-        ("floor_qk", "no arithmetic: Q/K in place, no barrier", probe(0), qk_bytes),
+        ("floor_phase", "no arithmetic: Q/K in place, each wave waits for all its loads, then "
+                        "a workgroup barrier, then the stores", probe(2), qk_bytes),
+        ("floor_wave", "no arithmetic: Q/K in place, each wave waits for all its loads before "
+                       "its first store", probe(5), qk_bytes),
+        ("floor_wave_uncapped", "floor_wave without the residency cap (all the waves the "
+                                "registers allow)", probe(5, cap=0), qk_bytes),
+        ("floor_qk", "no arithmetic: Q/K in place, each store as soon as its load arrives",
+         probe(0), qk_bytes),
         ("read_only", "the Q/K loads alone", probe(3), qk_bytes // 2),
         ("write_only", "the Q/K stores alone (zeros)", probe(4), qk_bytes // 2),
     ]

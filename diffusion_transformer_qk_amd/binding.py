@@ -50,7 +50,8 @@ class KernelInfo(ctypes.Structure):
     _fields_ = [("num_vgprs", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("scratch_bytes", ctypes.c_int32), ("block_threads", ctypes.c_int32),
                 ("tokens_per_block", ctypes.c_int32), ("heads_in_flight", ctypes.c_int32),
-                ("die_runs", ctypes.c_int32)]
+                ("die_runs", ctypes.c_int32), ("dynamic_lds_bytes", ctypes.c_int32),
+                ("workgroups_per_cu", ctypes.c_int32)]
 
 
 _lib = None

@@ -346,7 +346,10 @@ void qknorm_rope_kernel(const Params p)
     __shared__ float stage[PER_HEAD ? 4 : WAVES * 2 * D];   // [token][cos | sin][D]
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    // The wave index is uniform across the wave; saying so keeps the token,
+    // the tensor and its row and weight pointers in scalar registers (a
+    // per-lane index into the kernel arguments would be a memory load).
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     const int two = p.n_tensors == 2 ? 1 : 0;
     const int tokens_per_block = WAVES >> two;
@@ -457,6 +460,13 @@ constexpr int kBlock = kWavesPerBlock * kWave;
 constexpr int kNonTemporal = 3;         // Q/K loads and stores are not retained in cache
 constexpr int kUnrollPerHeadMax = 10;   // per-head layout also keeps 2 table rows per head
 constexpr int kDieRunsFromBlocks = 4096;
+// Residency cap: dynamic LDS (never touched by the kernel) that, with the
+// kernel's 2-8 KB of staging, takes 58-64 KB per workgroup, so that a
+// 160 KB CU holds 2 workgroups (8 waves) of the pass at a time.
+constexpr int kCapFromBlocks = 4096;
+constexpr int64_t kCapFromFlightBytes = 6144;
+constexpr size_t kCapLdsBytes = 56 * 1024;
+constexpr int kCapWorkgroupsPerCu = 2;
 
 // ---------------------------------------------------------------- dispatch
 //
@@ -469,7 +479,17 @@ constexpr int kDieRunsFromBlocks = 4096;
 //   order   one contiguous run of tokens per die when one buffer is streamed
 //           (fused QKV or a single tensor) and the grid has at least
 //           kDieRunsFromBlocks workgroups; hardware order otherwise (two
-//           separate q/k buffers, or small grids where per-die runs are short).
+//           separate q/k buffers, or small grids where per-die runs are short);
+//   residency  2 workgroups per CU (kCapLdsBytes of dynamic LDS) for the
+//           shared layout when the grid has at least kCapFromBlocks
+//           workgroups and each wave keeps at least kCapFromFlightBytes of
+//           Q/K loads in flight.  More resident waves make the HBM stream
+//           slower: on the 32760 x 3*40*128 fused call, 6 / 5 / 4 / 3 / 2 / 1
+//           workgroups per CU took 235.9 / 234.1 / 228.9 / 227.9 / 223.4 /
+//           313 us; on 75600 tokens 542.8 us uncapped, 502.3 us at 2.  Short
+//           grids and small slices need every wave they can get (the 5-head
+//           shard: 33.4 us uncapped, 67.7 us at 2), and the per-head layout's
+//           registers already hold it to 2-3 waves per SIMD.
 
 using KernelFn = void (*)(Params);
 
@@ -478,6 +498,8 @@ struct Launch {
     int order;
     int64_t blocks;
     int tokens_per_block;
+    size_t dynamic_lds;        // bytes of dynamic LDS per workgroup (the residency cap)
+    int workgroups_per_cu;     // the cap it sets, 0 for none
 };
 
 Launch plan_launch(int head_dim, int heads, int64_t tokens, int n_tensors, bool separate_pair,
@@ -492,6 +514,11 @@ Launch plan_launch(int head_dim, int heads, int64_t tokens, int n_tensors, bool 
     l.tokens_per_block = kWavesPerBlock / n_tensors;
     l.blocks = (tokens + l.tokens_per_block - 1) / l.tokens_per_block;
     l.order = (!separate_pair && l.blocks >= kDieRunsFromBlocks) ? -1 : 0;
+    const int heads_in_flight = heads < l.unroll * heads_per_iter ? heads : l.unroll * heads_per_iter;
+    const int64_t flight_bytes = (int64_t)heads_in_flight * head_dim * 2;
+    const bool cap = !per_head && l.blocks >= kCapFromBlocks && flight_bytes >= kCapFromFlightBytes;
+    l.dynamic_lds = cap ? kCapLdsBytes : 0;
+    l.workgroups_per_cu = cap ? kCapWorkgroupsPerCu : 0;
     return l;
 }
 
@@ -669,7 +696,8 @@ extern "C" int qknorm_rope_fused(void* qkv, void* q, void* k, int64_t tokens, in
     KernelFn fn = select_kernel(head_dim, style, cos_layout, cos_dtype, dtype, l);
     void* args[] = {&p};
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)l.blocks),
-                                     dim3(kBlock), args, 0, static_cast<hipStream_t>(stream));
+                                     dim3(kBlock), args, l.dynamic_lds,
+                                     static_cast<hipStream_t>(stream));
     return err == hipSuccess ? QKR_OK : QKR_ERR_HIP;
 }
 
@@ -719,5 +747,7 @@ extern "C" int qknorm_rope_kernel_info(int32_t head_dim, int32_t heads, int64_t 
     out->tokens_per_block = l.tokens_per_block;
     out->heads_in_flight = l.unroll;
     out->die_runs = l.order < 0 ? 1 : 0;
+    out->dynamic_lds_bytes = (int32_t)l.dynamic_lds;
+    out->workgroups_per_cu = l.workgroups_per_cu;
     return QKR_OK;
 }

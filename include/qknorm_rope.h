@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define QKNORM_ROPE_VERSION 1
+#define QKNORM_ROPE_VERSION 2
 
 /* Return codes.  On any error nothing is enqueued and no buffer is touched. */
 enum {
@@ -93,6 +93,12 @@ enum { QKR_ROPE_INTERLEAVED = 0, QKR_ROPE_ROTATE_HALF = 1 };
  * dtype       QKR_BF16 or QKR_FP16: element type of qkv / q / k.
  * stream      a hipStream_t (NULL = the default stream).
  *
+ * Long calls of the shared layout (at least 4096 workgroups, each wave
+ * keeping at least 6 KB of Q/K loads in flight) reserve 56 KB of LDS per
+ * workgroup at launch, which holds a CU to 2 of the pass's workgroups: the
+ * HBM stream runs faster with fewer waves resident (qknorm_rope_kernel_info
+ * reports it).  Kernels of other streams share what the pass leaves free.
+ *
  * Every data pointer must be 16-byte aligned.  The tensors written (qkv, or q
  * and k) must not overlap each other, gamma, cos or sin (QKR_ERR_ARG).
  * Returns QKR_OK or a negative QKR_ERR_* code; all checks happen before any
@@ -118,6 +124,10 @@ typedef struct {
     int32_t tokens_per_block; /* tokens one workgroup covers                      */
     int32_t heads_in_flight;  /* head iterations whose loads a lane keeps in flight */
     int32_t die_runs;         /* 1: each die processes one contiguous token run   */
+    int32_t dynamic_lds_bytes; /* LDS reserved per workgroup at launch (unused by  */
+                              /* the kernel) to cap residency; 0 for none          */
+    int32_t workgroups_per_cu; /* the residency that reservation allows on a      */
+                              /* 160 KB-LDS CU; 0 when not capped                  */
 } qkr_kernel_info;
 
 /* Which tensors a call passes, for qknorm_rope_kernel_info. */

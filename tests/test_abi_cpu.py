@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_strerror():
-    assert qkr.version() == 1
+    assert qkr.version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert qkr.strerror(code) != "unknown status"
     assert qkr.strerror(12345) == "unknown status"

@@ -68,16 +68,19 @@ def test_graph_and_flush_modes(mode):
     assert f["pct_of_peak_median"] > 0
 
 
-def test_floor_report():
+@pytest.mark.parametrize("extra", [(), ("--workload", "flux", "--flush")])
+def test_floor_report(extra):
     """--op floor times the pass beside its no-arithmetic access-pattern
-    probes (a library of their own) in two rounds; the pass cannot beat the
-    probe that moves the same bytes the same way."""
-    r = run_bench("--op", "floor", "--steps", "10", "--warmup", "2")
+    probes (a library of their own) in two rounds, for a fused buffer and
+    for separate q and k with flushed caches; the pass cannot beat the probe
+    that moves the same bytes the same way."""
+    r = run_bench("--op", "floor", "--steps", "10", "--warmup", "2", *extra)
     legs = set(r["legs"])
-    assert legs == {"pass", "floor_table", "floor_qk", "floor_flat", "copy"}
+    want = {"pass", "floor_table", "floor_phase", "floor_wave", "floor_wave_uncapped",
+            "floor_qk", "read_only", "write_only", "copy"}
+    assert legs == (want if extra else want | {"floor_flat"})
     assert len(r["rounds"]) == 2 and all(set(x) == legs for x in r["rounds"])
-    b = r["best_back_to_back_us"]
+    b = r["best_us"]
     assert all(v > 0 for v in b.values())
     assert r["value"] == round(b["pass"] / b["floor_table"], 4)
     assert r["value"] > 0.9
-

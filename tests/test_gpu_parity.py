@@ -167,7 +167,8 @@ def test_kernels_do_not_spill(head_dim, layout):
 def test_kernel_info_follows_the_tensors_passed():
     """The schedule kernel_info reports for each way of passing the tensors:
     two tokens per workgroup for fused QKV or a q, k pair, four for a single
-    tensor; per-die token runs for one streamed buffer only."""
+    tensor; per-die token runs for one streamed buffer only; the residency
+    cap for long grids of the shared layout with >= 6 KB in flight per wave."""
     args = (128, "shared", qkr.binding.QKR_FP32, "interleaved", qkr.binding.QKR_BF16)
     fused = qkr.kernel_info(*args, heads=40, tokens=100000, tensors="fused")
     pair = qkr.kernel_info(*args, heads=40, tokens=100000, tensors="pair")
@@ -178,6 +179,17 @@ def test_kernel_info_follows_the_tensors_passed():
     assert fused["heads_in_flight"] == pair["heads_in_flight"] == one["heads_in_flight"] == 10
     small = qkr.kernel_info(*args, heads=40, tokens=1000, tensors="one")
     assert small["die_runs"] == 0
+    # residency cap: long grids whose waves keep >= 6 KB of loads in flight
+    for info in (fused, pair, one):
+        assert (info["workgroups_per_cu"], info["dynamic_lds_bytes"]) == (2, 56 * 1024), info
+    assert small["workgroups_per_cu"] == small["dynamic_lds_bytes"] == 0
+    few_heads = qkr.kernel_info(*args, heads=5, tokens=100000, tensors="fused")
+    assert few_heads["workgroups_per_cu"] == 0
+    per_head = qkr.kernel_info(128, "per_head", qkr.binding.QKR_FP32, "interleaved",
+                               qkr.binding.QKR_BF16, heads=40, tokens=100000, tensors="fused")
+    assert per_head["workgroups_per_cu"] == 0
+    assert qkr.kernel_info(*args, heads=24, tokens=8192, tensors="fused")["workgroups_per_cu"] == 2
+    assert qkr.kernel_info(*args, heads=24, tokens=8190, tensors="fused")["workgroups_per_cu"] == 0
 
 
 # ----------------------------------------------------------------------------- the five workloads
