@@ -28,6 +28,17 @@ __device__ __forceinline__ float dpp(float v)
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+// The same move for a control under which every lane reads a lane of its own
+// row (a rotation or permutation within the row): no lane keeps an old value,
+// so none is supplied, and the compiler may fold the move into the
+// instruction that consumes it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_in_row(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 template <bool NT>
 __device__ __forceinline__ u32x4 load16(const void* p)
 {

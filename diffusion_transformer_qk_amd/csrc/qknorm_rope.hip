@@ -105,7 +105,7 @@ __device__ __forceinline__ float half_head_partner(float v)
     if constexpr (L == 32)
         return lane_xor16(v);
     else if constexpr (L == 16)
-        return dpp<0x128>(v);  // row_ror:8 == lane ^ 8 inside a 16-lane row
+        return dpp_in_row<0x128>(v);  // row_ror:8 == lane ^ 8 inside a 16-lane row
     else
         return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
                                                                      0x101F));  // lane ^ 4
