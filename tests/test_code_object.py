@@ -115,7 +115,10 @@ def waves_per_simd(vgprs: int) -> int:
 
 def test_headline_kernel_occupancy(kernels):
     """The fused-QKV interleaved bf16 kernel with 10 heads in flight and die
-    runs keeps at least 5 waves per SIMD (20 per CU, 5 workgroups)."""
+    runs leaves room for at least 5 waves per SIMD by its registers.  Its
+    long launches hold 2 workgroups per CU through an LDS reservation; the
+    register headroom keeps that a choice of the launch, not of the
+    allocation."""
     match = [k for k in kernels if "qknorm_rope_kernel" in k[".name"]
              and "ILi128ELi0ELb0ELb0ELb0ELi10ELi4ELi3ELin1E" in k[".name"]]
     assert len(match) == 1
