@@ -629,10 +629,15 @@ def test_misaligned_pointer_is_rejected_and_nothing_changes():
 # ----------------------------------------------------------------------------- capture and streams
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("T,H", [(97, 6), (8200, 40)])
+def test_graph_capture_replays_match_eager(T, H):
     """The call holds no allocation, copy or synchronisation, so it captures into a
-    HIP graph; every replay must equal the same number of eager calls, bit for bit."""
-    T, H, D = 97, 6, 128
+    HIP graph; every replay must equal the same number of eager calls, bit for bit.
+    8200 tokens of 40 heads is a long grid: its launch carries the residency
+    reservation of dynamic LDS into the graph node."""
+    D = 128
+    info = qkr.kernel_info(D, heads=H, tokens=T)
+    assert info["workgroups_per_cu"] == (2 if T == 8200 else 0), info
     qkv = wl.fused_qkv(100, T, H, D, "bf16")
     qg, kg = wl.norm_weights(100, D)
     cos, sin = tables(np.arange(T), (D // 2,), D, "interleaved")
