@@ -649,6 +649,145 @@ def bench_eager_chain(args):
 FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
 
 
+def _floor_lib():
+    """bench_floor.so with its one entry point typed."""
+    import ctypes
+    if not os.path.exists(FLOOR_LIB):
+        raise RuntimeError("bench_floor.so is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(FLOOR_LIB)
+    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    lib.qkr_floor.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp, u32, i32, i32, vp, vp]
+    lib.qkr_floor.restype = ctypes.c_int
+    return lib
+
+
+def _run_floor_legs(legs, stream, args, dev):
+    """Two rounds of every (key, what, launch, bytes) leg, the second in
+    reverse order; returns (rounds, best µs per leg)."""
+    import numpy as np
+    flush = CacheFlush(args.flush_mode, dev) if args.flush else None
+    rounds = []
+    for order in (legs, legs[::-1]):
+        res = {}
+        for key, _, launch, nbytes in order:
+            per, region_ms, _ = time_launches(launch, stream, args.steps, args.warmup, flush)
+            us = float(per.mean()) if flush else region_ms * 1e3 / args.steps
+            res[key] = {"us": round(us, 2), "mean_us": round(float(per.mean()), 2),
+                        "median_us": round(float(np.median(per)), 2),
+                        "pct_of_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2)}
+        rounds.append(res)
+    best = {k: min(r[k]["us"] for r in rounds) for k, _, _, _ in legs}
+    return rounds, best
+
+
+def bench_floor_steps(args):
+    """The AdaLN or group-norm step beside out-of-place probes of its bytes
+    (bench_floor.so mode 6: the x bytes read and written to a second buffer
+    by one wave per row of heads * 128 elements, no arithmetic), with and
+    without the QK pass's residency rule, the x bytes read alone and written
+    alone, and a plain device copy; two rounds, one stream.  Rows are the
+    step's own rows for AdaLN (hidden = heads * 128) and 4096-element slices
+    of x for group norm.  Prints one JSON line; `value` is the step's time
+    over the faster out-of-place probe's."""
+    import torch
+
+    import diffusion_transformer_qk_amd as qkr
+    import workloads as wl
+    lib = _floor_lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+    dtype = args.dtype
+    if args.workload in wl.ADALN_WORKLOADS:
+        w = wl.ADALN_WORKLOADS[args.workload]
+        dtype = dtype or w.dtypes[0]
+        x_cpu, sc, sh = wl.adaln_inputs(w.seed, w.rows, w.hidden, w.batches, dtype, args.mod_dtype)
+        x = x_cpu.to(dev)
+        scd, shd = sc.to(dev), sh.to(dev)
+        y = torch.empty_like(x)
+        nbytes = wl.adaln_bytes(w.rows, w.hidden, w.batches,
+                                mod_bytes=4 if args.mod_dtype == "fp32" else 2)
+        rows, width = w.rows, w.hidden
+        desc = "%s: x %s [%d, %d], %d modulation row(s) %s" % (w.key, dtype, w.rows, w.hidden,
+                                                             w.batches, args.mod_dtype)
+
+        def the_pass():
+            qkr.fuse_scale_shift(x, scd, shd, out=y, eps=wl.EPS, stream=handle)
+    else:
+        w = wl.GN_WORKLOADS[args.workload]
+        dtype = dtype or w.dtypes[0]
+        x_cpu, g, b = wl.gn_inputs(w.seed, w.n, w.channels, w.spatial, dtype, args.mod_dtype)
+        x = x_cpu.to(dev).view(w.n, w.channels, w.height, w.width)
+        gd, bd = g.to(dev), b.to(dev)
+        y = torch.empty_like(x)
+        need = qkr.group_norm_silu_workspace_size(w.n, w.channels, w.spatial, w.groups)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        nbytes = wl.gn_bytes(w.n, w.channels, w.spatial,
+                             param_bytes=4 if args.mod_dtype == "fp32" else 2)
+        width = 4096
+        rows = x.numel() // width
+        desc = "%s: x %s [%d, %d, %d, %d], %d groups, %s affine" % (
+            w.key, dtype, w.n, w.channels, w.height, w.width, w.groups, args.mod_dtype)
+
+        def the_pass():
+            qkr.group_norm_silu(x, gd, bd, w.groups, out=y, eps=wl.EPS, workspace=ws,
+                                stream=handle)
+    heads = width // 128
+    if width % 128 or heads > 48 or x.numel() != rows * width:
+        raise ValueError("the out-of-place probes take rows of at most 48 x 128 elements")
+    src = x.reshape(rows, width).clone()
+    dst = torch.empty_like(src)
+    scratch = src.clone()
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    x_bytes = rows * width * 2
+    magic = 0x9E3779B9
+
+    def probe(mode, buf, cap=1, out=None):
+        def launch():
+            rc = lib.qkr_floor(buf.data_ptr(), None, rows, heads, width, None, None,
+                               sink.data_ptr(), magic, mode, cap,
+                               out.data_ptr() if out is not None else None, handle)
+            if rc != 0:
+                raise RuntimeError("qkr_floor returned %d" % rc)
+        return launch
+
+    def copy():
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+
+    legs = [
+        ("pass", "the step (%s)" % ("fuse_scale_shift" if args.workload in wl.ADALN_WORKLOADS
+                                    else "group_norm_silu"), the_pass, nbytes),
+        ("floor_oop", "no arithmetic: x read, written to a second buffer, the pass's "
+                      "residency rule", probe(6, src, 1, dst), 2 * x_bytes),
+        ("floor_oop_uncapped", "floor_oop without the residency cap", probe(6, src, 0, dst),
+         2 * x_bytes),
+        ("read_only", "the x bytes read alone", probe(3, src), x_bytes),
+        ("write_only", "the x bytes written alone (zeros, into a scratch copy)",
+         probe(4, scratch), x_bytes),
+        ("copy", "device copy of the x bytes (torch copy_)", copy, 2 * x_bytes),
+    ]
+    rounds, best = _run_floor_legs(legs, stream, args, dev)
+    floor = min(best["floor_oop"], best["floor_oop_uncapped"])
+    result = {
+        "metric": "step time over an out-of-place stream of the same bytes",
+        "value": round(best["pass"] / floor, 4), "unit": "x",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": desc + ((", cache flushed (%s)" % args.flush_mode)
+                                       if args.flush else ""),
+                   "probe_rows": rows, "probe_row_elements": width,
+                   "timing": "mean per call, caches flushed before each" if args.flush
+                             else "back to back", "parallelism": "single GPU"},
+        "legs": {k: {"what": what, "bytes": b} for k, what, _, b in legs},
+        "rounds": rounds,
+        "best_us": best,
+        "read_then_write_us": round(best["read_only"] + best["write_only"], 2),
+    }
+    print(json.dumps(result))
+    return 0
+
+
 def bench_floor(args):
     """The pass beside data-movement probes of its access pattern
     (bench_floor.hip, a library of its own) on one workload, in one process
@@ -664,20 +803,14 @@ def bench_floor(args):
     floor_wave_uncapped applies the pass's residency rule.  Back-to-back time per call,
     or with --flush the mean per-call time with the caches evicted before
     each call.  Prints one JSON line; `value` is the pass's time over
-    floor_table's."""
-    import ctypes
-
-    import numpy as np
+    floor_table's.  An AdaLN or group-norm workload runs bench_floor_steps."""
     import torch
 
     import diffusion_transformer_qk_amd as qkr
     import workloads as wl
-    if not os.path.exists(FLOOR_LIB):
-        raise RuntimeError("bench_floor.so is not built; run __graft_entry__.build()")
-    lib = ctypes.CDLL(FLOOR_LIB)
-    vp, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
-    lib.qkr_floor.argtypes = [vp, vp, i64, i32, i64, vp, vp, vp, u32, i32, i32, vp]
-    lib.qkr_floor.restype = ctypes.c_int
+    if args.workload in wl.ADALN_WORKLOADS or args.workload in wl.GN_WORKLOADS:
+        return bench_floor_steps(args)
+    lib = _floor_lib()
     w = wl.WORKLOADS[args.workload or "headline"]
     style = args.style or w.styles[0]
     dtype = args.dtype or w.dtypes[0]
@@ -715,7 +848,7 @@ def bench_floor(args):
 
         def launch():
             rc = lib.qkr_floor(b0, b1, T, H, st, c.data_ptr(), s.data_ptr(), sink.data_ptr(),
-                               magic, mode, cap, handle)
+                               magic, mode, cap, None, handle)
             if rc != 0:
                 raise RuntimeError("qkr_floor returned %d" % rc)
         return launch
@@ -750,18 +883,7 @@ def bench_floor(args):
                      qk_bytes))
     legs.append(("copy", "device copy of the Q/K bytes (torch copy_, %d B each way)"
                  % (qk_bytes // 2), copy, qk_bytes))
-    flush = CacheFlush(args.flush_mode, dev) if args.flush else None
-    rounds = []
-    for order in (legs, legs[::-1]):
-        res = {}
-        for key, _, launch, nbytes in order:
-            per, region_ms, _ = time_launches(launch, stream, args.steps, args.warmup, flush)
-            us = float(per.mean()) if flush else region_ms * 1e3 / args.steps
-            res[key] = {"us": round(us, 2), "mean_us": round(float(per.mean()), 2),
-                        "median_us": round(float(np.median(per)), 2),
-                        "pct_of_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / PEAK_GBS, 2)}
-        rounds.append(res)
-    best = {k: min(r[k]["us"] for r in rounds) for k, _, _, _ in legs}
+    rounds, best = _run_floor_legs(legs, stream, args, dev)
     result = {
         "metric": "pass time over the data-movement floor of its access pattern",
         "value": round(best["pass"] / best["floor_table"], 4), "unit": "x",

@@ -1,5 +1,6 @@
 // bench_floor.hip -- data-movement floors of the fused QK-norm + RoPE pass's
-// access pattern on gfx950.  Measurement only: bench.py (--op floor) times
+// access pattern on gfx950 (and, out of place, of the row-wise AdaLN and
+// group-norm steps' bytes).  Measurement only: bench.py (--op floor) times
 // these probes beside the pass; they are built into their own library
 // (bench_floor.so), never into libqknorm_rope.so.
 //
@@ -23,8 +24,12 @@
 //      sink only if it equals a value the host never passes as `magic`;
 //   4  stores only: each vector written with zeros (the data is destroyed);
 //   5  mode 0, but every wave waits for all of its loads before its first
-//      store (no barrier).
-// Modes 2 and 5 make the stores depend on every loaded vector through the
+//      store (no barrier);
+//   6  mode 5 out of place: the vectors read from a single tensor are
+//      written to the same positions of another buffer y (the access
+//      pattern of a row-wise step that writes a new tensor, such as the
+//      AdaLN modulation, when heads * 128 is its row width).
+// Modes 2, 5 and 6 make the stores depend on every loaded vector through the
 // same fold as mode 3: the data written equals the data read unless the fold
 // equals `magic`.
 //
@@ -57,6 +62,7 @@ struct FloorParams {
     const float* cos;
     const float* sin;
     uint32_t* sink;            // mode 3
+    uint16_t* y;               // mode 6: the destination, laid out like x[0]
     int64_t row_stride;
     int64_t tokens;
     int32_t heads;
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void floor_kernel(const FloorParams p)
                 acc = fmaxf(acc, sn[i]);
             flip = acc > 4.0f ? 1u : 0u;              // |cos|, |sin| <= 1: never set
         }
-    } else if constexpr (MODE == 2 || MODE == 5) {
+    } else if constexpr (MODE == 2 || MODE == 5 || MODE == 6) {
         if (active) {
             uint32_t acc = 0;
 #pragma unroll
@@ -141,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void floor_kernel(const FloorParams p)
             p.sink[0] = acc;
         return;
     }
+    uint16_t* const dst = MODE == 6 ? p.y + t * p.row_stride : row;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int h = u * kHpi + hs;
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void floor_kernel(const FloorParams p)
             if constexpr (MODE == 4)
                 store16<true>(row + h * kD + d0, u32x4{0, 0, 0, 0});
             else
-                store16<true>(row + h * kD + d0, v[u] ^ flip);
+                store16<true>(dst + h * kD + d0, v[u] ^ flip);
         }
     }
 }
@@ -164,6 +171,7 @@ FloorFn pick_mode(int mode, bool runs)
     case 3: return runs ? floor_kernel<U, 3, -1> : floor_kernel<U, 3, 0>;
     case 4: return runs ? floor_kernel<U, 4, -1> : floor_kernel<U, 4, 0>;
     case 5: return runs ? floor_kernel<U, 5, -1> : floor_kernel<U, 5, 0>;
+    case 6: return runs ? floor_kernel<U, 6, -1> : floor_kernel<U, 6, 0>;
     default: return runs ? floor_kernel<U, 0, -1> : floor_kernel<U, 0, 0>;
     }
 }
@@ -175,28 +183,32 @@ FloorFn pick_mode(int mode, bool runs)
 // buffer x1 = x0 + heads * 128), rows row_stride elements apart, on `stream`.
 // cos/sin: fp32 [tokens, 128], read in mode 1 only; sink: one device word,
 // written in mode 3 only (and only if a wave's folded data equals magic).
-// cap: 1 applies the pass's residency rule, 0 never reserves LDS.
+// cap: 1 applies the pass's residency rule, 0 never reserves LDS.  y: mode
+// 6's destination, tokens * row_stride elements that do not overlap x0
+// (NULL in the other modes); mode 6 takes a single tensor (x1 == NULL).
 // Returns 0, or -1 (NULL pointer), -2 (sizes: tokens < 1 or >= 2^24, heads
 // not in 1..48, row_stride < heads * 128 for separate tensors or
-// < 2 * heads * 128 for a fused buffer, mode not in 0..5, cap not 0 or 1),
-// -3 (pointer not 16-byte aligned), -6 (launch failed).
+// < 2 * heads * 128 for a fused buffer, mode not in 0..6, cap not 0 or 1,
+// mode 6 with x1), -3 (pointer not 16-byte aligned), -6 (launch failed).
 extern "C" int qkr_floor(void* x0, void* x1, int64_t tokens, int32_t heads, int64_t row_stride,
                          const float* cos, const float* sin, uint32_t* sink, uint32_t magic,
-                         int32_t mode, int32_t cap, void* stream)
+                         int32_t mode, int32_t cap, void* y, void* stream)
 {
-    if (!x0 || (mode == 1 && (!cos || !sin)) || (mode == 3 && !sink))
+    if (!x0 || (mode == 1 && (!cos || !sin)) || (mode == 3 && !sink) || (mode == 6 && !y))
         return -1;
     const bool fused = x1 && static_cast<uint16_t*>(x1) == static_cast<uint16_t*>(x0) + (int64_t)heads * kD;
     if (tokens < 1 || tokens >= ((int64_t)1 << 24) || heads < 1 || heads > 12 * kHpi ||
-        mode < 0 || mode > 5 || (cap != 0 && cap != 1) ||
+        mode < 0 || mode > 6 || (cap != 0 && cap != 1) || (mode == 6 && x1) ||
         row_stride < (fused ? 2 : 1) * (int64_t)heads * kD)
         return -2;
     const uintptr_t bits = reinterpret_cast<uintptr_t>(x0) | reinterpret_cast<uintptr_t>(x1) |
-                           (mode == 1 ? reinterpret_cast<uintptr_t>(cos) | reinterpret_cast<uintptr_t>(sin) : 0);
+                           (mode == 1 ? reinterpret_cast<uintptr_t>(cos) | reinterpret_cast<uintptr_t>(sin) : 0) |
+                           (mode == 6 ? reinterpret_cast<uintptr_t>(y) : 0);
     if ((bits & 15u) || (row_stride % kVec))
         return -3;
     FloorParams p = {{static_cast<uint16_t*>(x0), static_cast<uint16_t*>(x1 ? x1 : x0)},
-                     cos, sin, sink, row_stride, tokens, heads, x1 ? 2 : 1, magic};
+                     cos, sin, sink, static_cast<uint16_t*>(y), row_stride, tokens, heads, x1 ? 2 : 1,
+                     magic};
     const int tokens_per_block = kWaves / p.n_tensors;
     const int64_t blocks = (tokens + tokens_per_block - 1) / tokens_per_block;
     // one run of tokens per die when one buffer is streamed, as the pass does

@@ -84,3 +84,19 @@ def test_floor_report(extra):
     assert all(v > 0 for v in b.values())
     assert r["value"] == round(b["pass"] / b["floor_table"], 4)
     assert r["value"] > 0.9
+
+
+@pytest.mark.parametrize("workload", ["adaln_wan", "gn_vae_out"])
+def test_floor_report_for_the_row_steps(workload):
+    """--op floor on an AdaLN or group-norm workload times the step beside
+    out-of-place probes of its bytes (capped and uncapped), the bytes read
+    alone and written alone, and a device copy."""
+    r = run_bench("--op", "floor", "--workload", workload, "--steps", "10", "--warmup", "2")
+    legs = set(r["legs"])
+    assert legs == {"pass", "floor_oop", "floor_oop_uncapped", "read_only", "write_only", "copy"}
+    assert len(r["rounds"]) == 2 and all(set(x) == legs for x in r["rounds"])
+    b = r["best_us"]
+    assert all(v > 0 for v in b.values())
+    assert r["value"] == round(b["pass"] / min(b["floor_oop"], b["floor_oop_uncapped"]), 4)
+    assert r["value"] > 0.8
+
